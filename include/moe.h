@@ -1,0 +1,208 @@
+/*
+ * moe.h -- C ABI of a single-GPU MoE expert layer for AMD Instinct MI355X
+ * (gfx950): softmax top-k routing, permute into per-expert groups, grouped
+ * SwiGLU GEMM (forward, backward dX, backward dW), unpermute + gate-weighted
+ * combine, and the backward of each step.
+ *
+ * Sources, cited by page title and section:
+ *  [CANN-MoE]  "MoE算子优化：动态路由硬件加速与零拷贝通信实践" (gtnt.cn):
+ *              s2.1 routing = Softmax -> Top-k -> mask; s2.2 experts are
+ *              fully-connected layers computed tile by tile; s4.2 router FP32.
+ *  [MoE-ops]   Huawei MoE training operator article (feedman.me): VectorSort
+ *              section, Fig. 3 (reorder / anti-reorder of tokens); Host-Device
+ *              section, Fig. 4 (token-dispatch preprocessing without a host wait).
+ *  [Pangu-QA]  QbitAI article on the Pangu Ultra MoE report (rjtj.cn):
+ *              dropless training; expert backward split into dW and dX;
+ *              experimental results (output = weighted sum of shared and
+ *              routed experts).
+ *  [MindSpore-DSv3] "昇思MindSpore助力天翼云提供极致MoE大模型训练性能"
+ *              (mindspore.cn): 01.1 tokens sorted inside a machine; 03.3
+ *              GroupedMatmul over all experts.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless stated; tensors are dense row-major
+ *    and 16-byte aligned.  ``dt`` selects the storage type of token rows and
+ *    expert weights: MOE_F32 (fp32) or MOE_BF16 (bf16 bits, fp32 arithmetic
+ *    inside).  Router weights, logits, gates and their gradients are fp32.
+ *  - Every call only enqueues work on ``stream`` (a hipStream_t; NULL is the
+ *    null stream) and returns; none synchronises and none reads device data
+ *    back to the host, so no output size depends on the routing: permuted
+ *    buffers always have R = T*k rows (dropless, [Pangu-QA]).
+ *  - The caller owns every buffer, including workspaces.  The library keeps no
+ *    device memory; its only global state is the per-device CU count and the
+ *    thread-local text of the last error.
+ *  - Arguments are validated on the host before any launch.  Errors:
+ *    MOE_ERR_INVALID_ARG (null pointer, misalignment, negative or
+ *    inconsistent size), MOE_ERR_UNSUPPORTED (outside the supported shapes:
+ *    1 <= k <= E <= 1024, H and I multiples of 64, sizes below 2^31 elements
+ *    per tensor), MOE_ERR_WORKSPACE (workspace too small), MOE_ERR_LAUNCH (the
+ *    runtime rejected a launch).  T == 0 is a successful no-op.  Device data
+ *    is not checked: logits must be finite; offsets and row maps must come
+ *    from moe_permute.  Kernels clamp every row index to its buffer, so bad
+ *    device data gives wrong numbers, never an out-of-bounds access.
+ *  - Results are bitwise reproducible run to run (no floating-point atomics;
+ *    every reduction has a fixed order).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_LAUNCH = 4
+};
+
+/* Text for a status code; static storage. */
+const char* moe_status_string(int status);
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* moe_last_error(void);
+/* ABI version of this header (bumped on any signature change). */
+int moe_abi_version(void);
+
+/* ---------------------------------------------------------------- router
+ * Router projection, kept in fp32 ([CANN-MoE] s4.2):
+ *   logits[T,E] = x[T,H] . Wg[H,E] + bias[E]     (bias nullable)
+ * x has storage type dt and is widened to fp32; products accumulate in fp32.
+ */
+int moe_router_logits(const void* x, int dt, const float* wg, const float* bias,
+                      int T, int H, int E, float* logits, moe_stream_t stream);
+
+/* Backward of moe_router_logits:
+ *   dx[T,H]  = dlogits . Wg^T        (written, storage type dt)
+ *   dwg[H,E] = x^T . dlogits         (written, fp32)
+ *   dbias[E] = sum_t dlogits[t,:]    (written, fp32; nullable)
+ */
+int moe_router_logits_bwd(const float* dlogits, const void* x, int dt, const float* wg,
+                          int T, int H, int E, void* dx, float* dwg, float* dbias,
+                          moe_stream_t stream);
+
+/* ---------------------------------------------------------------- routing
+ * Softmax -> top-k -> selection ([CANN-MoE] s2.1), one token per wavefront:
+ *   idx[t,j]  = the j-th expert by descending fp32 logit; equal logits go
+ *               to the lower expert index (int32, [T,k])
+ *   gate[t,j] = softmax(logits[t,:])[idx[t,j]] (fp32, [T,k]; not
+ *               renormalised over the k chosen experts)
+ */
+int moe_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
+              moe_stream_t stream);
+
+/* Backward of the gate values (the selection has no gradient):
+ *   dlogits[t,e] = p[t,e] * (dp[t,e] - sum_j gate[t,j] dgate[t,j])
+ * with p = softmax(logits[t,:]) recomputed and dp = dgate at the chosen
+ * experts, 0 elsewhere.  dlogits is [T,E] fp32, fully written.
+ */
+int moe_route_bwd(const float* logits, const int32_t* idx, const float* dgate,
+                  int T, int E, int k, float* dlogits, moe_stream_t stream);
+
+/* ---------------------------------------------------------------- permute
+ * Reorder of tokens into contiguous per-expert groups ([MoE-ops] VectorSort,
+ * Fig. 3; the counts stay on the device, [MoE-ops] Host-Device section, Fig. 4):
+ *   counts[e]       number of (token, slot) pairs routed to e           [E]
+ *   offsets[e]      exclusive scan of counts; offsets[E] = T*k           [E+1]
+ *   row_id_map[t,j] row of pair (t,j): offsets[e] + number of tokens t' < t
+ *                   that chose e (rows of a group keep token order)      [T,k]
+ *   src_token[r]    token that row r came from                           [T*k]
+ *   xp[r,:]         = x[src_token[r],:], a bit copy                      [T*k,H]
+ * ws must hold moe_permute_workspace_bytes(T,E,k) bytes (contents scratch).
+ */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
+                void* xp, int32_t* counts, int32_t* offsets, int32_t* row_id_map,
+                int32_t* src_token, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Backward of the permute (adjoint of the row copy), fp32 sums:
+ *   dx[t,:] = sum_j dxp[row_id_map[t,j],:] + add0[t,:] + add1[t,:]
+ * add0/add1 are optional [T,H] tensors of type dt (nullable), e.g. the shared
+ * expert's and the router's input gradients.  dx is written.
+ */
+int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int dt, int T, int H, int k,
+                    const void* add0, const void* add1, void* dx, moe_stream_t stream);
+
+/* Anti-reorder and gate-weighted combine ([MoE-ops] VectorSort; [Pangu-QA]
+ * experimental results; the shared expert enters with weight 1):
+ *   y[t,:] = y_shared[t,:] + sum_{j=0..k-1} gate[t,j] * yp[row_id_map[t,j],:]
+ * summed in fp32 in ascending j; y_shared nullable.
+ */
+int moe_unpermute_combine(const void* yp, const int32_t* row_id_map, const float* gate,
+                          const void* y_shared, int dt, int T, int H, int k, void* y,
+                          moe_stream_t stream);
+
+/* Backward of moe_unpermute_combine:
+ *   dyp[row_id_map[t,j],:] = gate[t,j] * dy[t,:]          (all T*k rows written)
+ *   dgate[t,j]             = <dy[t,:], yp[row_id_map[t,j],:]>   (fp32)
+ */
+int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row_id_map,
+                              const float* gate, int dt, int T, int H, int k, void* dyp,
+                              float* dgate, moe_stream_t stream);
+
+/* ---------------------------------------------------------------- grouped GEMM
+ * GroupedMatmul SwiGLU experts ([MindSpore-DSv3] 03.3; [CANN-MoE] s2.2) over
+ * the groups g0 <= e < g0+G of a permuted buffer of R rows.  Group e owns
+ * rows [offsets[e], offsets[e+1]) (read on the device).  Expert weights are
+ * indexed e - g0 and stored whole per expert:
+ *   w13 [G,2I,H]: rows 0..I-1 gate projection, rows I..2I-1 up projection
+ *   w2  [G,H,I]
+ * Row indices into xp/h13/act/yp/... are absolute; rows of other groups are
+ * not touched (remote experts).  An optional shared expert runs on its own
+ * T rows in the same launch (a dense group with its own weights).
+ * Arithmetic: dt products, fp32 accumulation; outputs stored as dt.
+ */
+typedef struct moe_shared_expert {
+  int T;             /* rows of the shared expert (tokens) */
+  const void* x;     /* [T,H]  input rows (forward, dW) */
+  const void* w13;   /* [2I,H] */
+  const void* w2;    /* [H,I]  */
+  void* h13;         /* [T,2I] forward out; bwd_dx in */
+  void* act;         /* [T,I]  forward out; bwd_dw in */
+  void* y;           /* [T,H]  forward out */
+  const void* dy;    /* [T,H]  bwd_dx / bwd_dw in */
+  void* dh13;        /* [T,2I] bwd_dx out; bwd_dw in */
+  void* dx;          /* [T,H]  bwd_dx out */
+  void* dw13;        /* [2I,H] bwd_dw out */
+  void* dw2;         /* [H,I]  bwd_dw out */
+} moe_shared_expert;
+
+/* Forward:  h13 = xp . w13[e]^T        (saved, [R,2I])
+ *           act = silu(h13[:, :I]) * h13[:, I:]   (saved, [R,I]; silu(z) = z/(1+e^-z))
+ *           yp  = act . w2[e]^T        ([R,H])
+ * The activation is applied to the fp32 accumulators before rounding. */
+int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
+                         int dt, int H, int I, const void* w13, const void* w2,
+                         void* h13, void* act, void* yp, const moe_shared_expert* shared,
+                         moe_stream_t stream);
+
+/* Backward dX ([Pangu-QA]: dX is computed apart from dW):
+ *   dact = dyp . w2[e];  g = h13[:, :I], u = h13[:, I:], s = sigmoid(g)
+ *   dh13[:, :I] = dact * u * s * (1 + g (1 - s));  dh13[:, I:] = dact * g * s
+ *   dxp = dh13 . w13[e]                                   ([R,H])
+ */
+int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G, int R,
+                            int dt, int H, int I, const void* w13, const void* w2,
+                            const void* h13, void* dh13, void* dxp,
+                            const moe_shared_expert* shared, moe_stream_t stream);
+
+/* Backward dW, contraction over each group's rows (K = its row count):
+ *   dw2[e]  = dyp_e^T . act_e     ([G,H,I])
+ *   dw13[e] = dh13_e^T . xp_e     ([G,2I,H])
+ * A group with no rows gets exact zeros. */
+int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp, const void* dh13,
+                            const int32_t* offsets, int g0, int G, int R, int dt, int H, int I,
+                            void* dw13, void* dw2, const moe_shared_expert* shared,
+                            moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

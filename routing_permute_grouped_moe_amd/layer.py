@@ -1,0 +1,199 @@
+"""The MoE expert layer as a sequence of C-ABI calls on one GPU.
+
+This module only allocates device buffers (through torch) and calls the
+library entry points in order; every step of the layer runs in the HIP
+kernels of ``libmoe.so``.
+
+Forward:  router logits -> route -> permute -> grouped GEMM (+ shared expert)
+          -> unpermute/combine.
+Backward: combine bwd -> grouped GEMM dX -> grouped GEMM dW -> route bwd ->
+          router bwd -> permute bwd (which also adds the shared expert's and
+          the router's input gradients).
+
+Experts outside ``[g0, g0+G)`` are remote: their rows are moved by the
+permute and the combine, their expert outputs and input gradients are zero
+(the buffers are cleared once at allocation and never written), and they get
+no weight gradients.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from . import abi
+
+
+@dataclass
+class LayerShape:
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    dtype: torch.dtype          # torch.bfloat16 or torch.float32
+    g0: int = 0
+    G: Optional[int] = None     # experts run by the grouped GEMM (None = all E)
+    shared: bool = False
+    router: bool = True         # False: logits are an input
+
+    @property
+    def groups(self) -> int:
+        return self.E - self.g0 if self.G is None else self.G
+
+    @property
+    def R(self) -> int:
+        return self.T * self.k
+
+
+class MoeLayer:
+    """Device buffers of one layer plus the forward/backward call sequences."""
+
+    def __init__(self, shape: LayerShape, device="cuda"):
+        s = self.s = shape
+        dev = self.device = torch.device(device)
+        dt, f32, i32 = s.dtype, torch.float32, torch.int32
+        self.dt = abi.MOE_BF16 if dt == torch.bfloat16 else abi.MOE_F32
+        T, H, I, E, k, R, G = s.T, s.H, s.I, s.E, s.k, s.R, s.groups
+        e = lambda *shp, d=dt: torch.empty(shp, dtype=d, device=dev)
+        z = lambda *shp, d=dt: torch.zeros(shp, dtype=d, device=dev)
+        # parameters / inputs (filled by the caller)
+        self.x = e(T, H)
+        self.wg = e(H, E, d=f32) if s.router else None
+        self.bias = None
+        self.logits = e(T, E, d=f32)
+        self.w13 = e(G, 2 * I, H)
+        self.w2 = e(G, H, I)
+        self.ws13 = e(2 * I, H) if s.shared else None
+        self.ws2 = e(H, I) if s.shared else None
+        self.dy = e(T, H)
+        # forward state
+        self.idx = e(T, k, d=i32)
+        self.gate = e(T, k, d=f32)
+        self.xp = e(R, H)
+        self.counts = e(E, d=i32)
+        self.offsets = e(E + 1, d=i32)
+        self.row_id_map = e(T, k, d=i32)
+        self.src_token = e(R, d=i32)
+        self.ws_bytes = abi.moe_permute_workspace_bytes(T, E, k)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.h13 = e(R, 2 * I)
+        self.act = e(R, I)
+        self.yp = z(R, H)            # remote rows stay zero
+        self.y = e(T, H)
+        if s.shared:
+            self.sh_h13 = e(T, 2 * I)
+            self.sh_act = e(T, I)
+            self.ys = e(T, H)
+        # backward state
+        self.dyp = e(R, H)
+        self.dgate = e(T, k, d=f32)
+        self.dh13 = e(R, 2 * I)
+        self.dxp = z(R, H)           # remote rows stay zero
+        self.dw13 = e(G, 2 * I, H)
+        self.dw2 = e(G, H, I)
+        self.dlogits = e(T, E, d=f32)
+        self.dx = e(T, H)
+        if s.router:
+            self.dx_router = e(T, H)
+            self.dwg = e(H, E, d=f32)
+            self.dbias = e(E, d=f32)
+        if s.shared:
+            self.sh_dh13 = e(T, 2 * I)
+            self.sh_dx = e(T, H)
+            self.dws13 = e(2 * I, H)
+            self.dws2 = e(H, I)
+
+    # ------------------------------------------------------------------ helpers
+    def shared_desc(self):
+        if not self.s.shared:
+            return None
+        return abi.shared_expert(
+            T=self.s.T, x=self.x, w13=self.ws13, w2=self.ws2, h13=self.sh_h13, act=self.sh_act,
+            y=self.ys, dy=self.dy, dh13=self.sh_dh13, dx=self.sh_dx, dw13=self.dws13,
+            dw2=self.dws2)
+
+    # ------------------------------------------------------------------ steps
+    def router_fwd(self, stream=None):
+        s = self.s
+        abi.moe_router_logits(self.x, self.dt, self.wg, self.bias, s.T, s.H, s.E, self.logits,
+                              stream)
+
+    def route(self, stream=None):
+        s = self.s
+        abi.moe_route(self.logits, s.T, s.E, s.k, self.idx, self.gate, stream)
+
+    def permute(self, stream=None):
+        s = self.s
+        abi.moe_permute(self.x, self.dt, self.idx, s.T, s.H, s.E, s.k, self.xp, self.counts,
+                        self.offsets, self.row_id_map, self.src_token, self.ws, self.ws_bytes,
+                        stream)
+
+    def gmm_fwd(self, stream=None, shared=None):
+        s = self.s
+        sh = self.shared_desc() if shared is None else shared
+        abi.moe_grouped_gemm_fwd(self.xp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H, s.I,
+                                 self.w13, self.w2, self.h13, self.act, self.yp, sh, stream)
+
+    def combine(self, stream=None):
+        s = self.s
+        abi.moe_unpermute_combine(self.yp, self.row_id_map, self.gate,
+                                  self.ys if s.shared else None, self.dt, s.T, s.H, s.k, self.y,
+                                  stream)
+
+    def combine_bwd(self, stream=None):
+        s = self.s
+        abi.moe_unpermute_combine_bwd(self.dy, self.yp, self.row_id_map, self.gate, self.dt, s.T,
+                                      s.H, s.k, self.dyp, self.dgate, stream)
+
+    def gmm_bwd_dx(self, stream=None, shared=None):
+        s = self.s
+        sh = self.shared_desc() if shared is None else shared
+        abi.moe_grouped_gemm_bwd_dx(self.dyp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H,
+                                    s.I, self.w13, self.w2, self.h13, self.dh13, self.dxp, sh,
+                                    stream)
+
+    def gmm_bwd_dw(self, stream=None, shared=None):
+        s = self.s
+        sh = self.shared_desc() if shared is None else shared
+        abi.moe_grouped_gemm_bwd_dw(self.xp, self.act, self.dyp, self.dh13, self.offsets, s.g0,
+                                    s.groups, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh,
+                                    stream)
+
+    def route_bwd(self, stream=None):
+        s = self.s
+        abi.moe_route_bwd(self.logits, self.idx, self.dgate, s.T, s.E, s.k, self.dlogits, stream)
+
+    def router_bwd(self, stream=None):
+        s = self.s
+        abi.moe_router_logits_bwd(self.dlogits, self.x, self.dt, self.wg, s.T, s.H, s.E,
+                                  self.dx_router, self.dwg, self.dbias, stream)
+
+    def permute_bwd(self, stream=None):
+        s = self.s
+        abi.moe_permute_bwd(self.dxp, self.row_id_map, self.dt, s.T, s.H, s.k,
+                            self.sh_dx if s.shared else None,
+                            self.dx_router if s.router else None, self.dx, stream)
+
+    # ------------------------------------------------------------------ passes
+    def forward(self, stream=None):
+        if self.s.router:
+            self.router_fwd(stream)
+        self.route(stream)
+        self.permute(stream)
+        self.gmm_fwd(stream)
+        self.combine(stream)
+
+    def backward(self, stream=None):
+        self.combine_bwd(stream)
+        self.gmm_bwd_dx(stream)
+        self.gmm_bwd_dw(stream)
+        self.route_bwd(stream)
+        if self.s.router:
+            self.router_bwd(stream)
+        self.permute_bwd(stream)
+
+    def step(self, stream=None):
+        self.forward(stream)
+        self.backward(stream)

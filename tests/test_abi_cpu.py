@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before any GPU work (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "routing_permute_grouped_moe_amd", "libmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_layer_calls():
+    names = set(declared())
+    for n in ["moe_route", "moe_route_bwd", "moe_permute", "moe_permute_bwd",
+              "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd_dx", "moe_grouped_gemm_bwd_dw",
+              "moe_unpermute_combine", "moe_unpermute_combine_bwd", "moe_router_logits",
+              "moe_router_logits_bwd"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    from routing_permute_grouped_moe_amd import abi
+    assert sorted(abi.EXPORTED) == declared()
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from routing_permute_grouped_moe_amd import abi as a
+    return a
+
+
+FAKE = 0x10000        # an aligned address that is never dereferenced on these paths
+FAKE_ODD = 0x10002
+
+
+def status(abi, name, *args):
+    return getattr(abi._lib, name)(*args)
+
+
+def test_status_strings(abi):
+    assert abi.moe_status_string(0) == "ok"
+    assert abi.moe_status_string(3) == "workspace too small"
+    assert abi.moe_abi_version() >= 1
+
+
+def test_route_rejects_bad_k_and_e(abi):
+    assert status(abi, "moe_route", FAKE, 4, 8, 9, FAKE, FAKE, None) == abi.MOE_ERR_UNSUPPORTED
+    assert "k = 9" in abi.moe_last_error()
+    assert status(abi, "moe_route", FAKE, 4, 8, 0, FAKE, FAKE, None) == abi.MOE_ERR_UNSUPPORTED
+    assert status(abi, "moe_route", FAKE, 4, 2000, 2, FAKE, FAKE, None) == abi.MOE_ERR_UNSUPPORTED
+    assert "E = 2000" in abi.moe_last_error()
+
+
+def test_route_rejects_null_and_negative(abi):
+    assert status(abi, "moe_route", None, 4, 8, 2, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+    assert "logits is NULL" in abi.moe_last_error()
+    assert status(abi, "moe_route", FAKE, -1, 8, 2, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop(abi):
+    assert status(abi, "moe_route", None, 0, 8, 2, None, None, None) == abi.MOE_OK
+    assert status(abi, "moe_route_bwd", None, None, None, 0, 8, 2, None, None) == abi.MOE_OK
+    assert status(abi, "moe_unpermute_combine", None, None, None, None, 1, 0, 128, 2, None,
+                  None) == abi.MOE_OK
+    assert status(abi, "moe_permute_bwd", None, None, 1, 0, 128, 2, None, None, None,
+                  None) == abi.MOE_OK
+
+
+def test_permute_workspace(abi):
+    need = abi.moe_permute_workspace_bytes(100, 8, 2)
+    assert need >= 4 * 8 * ((100 + 31) // 32)
+    st = status(abi, "moe_permute", FAKE, 1, FAKE, 100, 128, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
+                FAKE, need - 4, None)
+    assert st == abi.MOE_ERR_WORKSPACE
+
+
+def test_shape_limits(abi):
+    # H not a multiple of 64
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 1, 4, 100, 2, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    # misaligned pointer
+    st = status(abi, "moe_unpermute_combine", FAKE_ODD, FAKE, FAKE, None, 1, 4, 128, 2, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG
+    # unknown dtype
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 7, 4, 128, 2, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG
+    # grouped GEMM: I not a multiple of 64, window beyond 1024 experts
+    st = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 0, 8, 64, 1, 128, 96, FAKE, FAKE, FAKE,
+                FAKE, FAKE, None, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    st = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 1000, 100, 64, 1, 128, 64, FAKE, FAKE,
+                FAKE, FAKE, FAKE, None, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    # a row longer than the row kernels keep in registers
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 0, 4, 16384, 2, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_raises_with_detail(abi):
+    with pytest.raises(abi.MoeError) as ei:
+        abi.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, stream=0)
+    assert ei.value.status == abi.MOE_ERR_UNSUPPORTED
+    assert "k = 9" in str(ei.value)

@@ -1,0 +1,288 @@
+"""Per-call parity of the HIP library against the CPU oracle (GPU only).
+
+Integer and index outputs are compared bit for bit; floating-point outputs by
+max|gpu - ref| <= tol * max|ref| per tensor, with tol = 1e-5 for fp32
+storage and 2e-2 for bf16 storage (fp32 accumulation in both).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev, have_gpu, host, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from routing_permute_grouped_moe_amd import abi as a
+    return a
+
+
+def _rng(i):
+    return np.random.default_rng(7000 + i)
+
+
+def _tdt(dt):
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def _code(abi, dt):
+    return abi.MOE_BF16 if dt == "bf16" else abi.MOE_F32
+
+
+def _store(a, dt):
+    return synth.bf16_round(np.asarray(a, np.float32)) if dt == "bf16" else np.asarray(a, np.float32)
+
+
+# ---------------------------------------------------------------- routing
+
+ROUTE_CASES = [(64, 8, 2, "normal"), (300, 64, 6, "normal"), (257, 256, 8, "ties"),
+               (100, 1024, 8, "normal"), (33, 1024, 1024, "normal"), (50, 1, 1, "normal"),
+               (70, 5, 5, "ties"), (129, 200, 3, "ties")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_bit_exact_indices(abi, T, E, k, kind):
+    r = _rng(T + E + k)
+    if kind == "ties":
+        logits = (r.integers(-3, 4, size=(T, E)) * 0.5).astype(np.float32)
+    else:
+        logits = r.standard_normal((T, E)).astype(np.float32) * 2
+    L = dev(logits, torch.float32)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    abi.moe_route(L, T, E, k, idx, gate)
+    torch.cuda.synchronize()
+    ridx, rgate = oracle.route(logits, k)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(gate), rgate) <= 1e-5
+    # backward
+    dgate = r.standard_normal((T, k)).astype(np.float32)
+    dl = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    abi.moe_route_bwd(L, idx, dev(dgate, torch.float32), T, E, k, dl)
+    torch.cuda.synchronize()
+    ref = oracle.route_backward(logits, ridx, dgate)
+    assert rel_err(host(dl), ref) <= 1e-5
+    assert np.abs(host(dl).astype(np.float64).sum(axis=1)).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+def test_route_deterministic(abi):
+    r = _rng(99)
+    T, E, k = 4096, 256, 8
+    L = dev(r.standard_normal((T, E)).astype(np.float32), torch.float32)
+    outs = []
+    for _ in range(2):
+        idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        gate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        abi.moe_route(L, T, E, k, idx, gate)
+        outs.append((idx.clone(), gate.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------- permute family
+
+PERM_CASES = [(1, 8, 2, 128, "f32"), (31, 8, 2, 128, "f32"), (33, 16, 4, 256, "bf16"),
+              (1000, 64, 6, 2048, "bf16"), (513, 256, 8, 7680, "bf16"), (40, 5, 5, 64, "f32"),
+              (2048, 1024, 16, 128, "bf16"), (100, 3, 1, 8192, "f32")]
+
+
+def _perm_inputs(T, E, k, H, dt, seed):
+    r = _rng(seed)
+    bias = np.where(np.arange(E) < max(1, E // 16), 3.0, 0.0)   # a few hot experts
+    logits = (r.standard_normal((T, E)) + bias).astype(np.float32)
+    idx, gate = oracle.route(logits, k)
+    x = _store(r.standard_normal((T, H)), dt)
+    return r, idx, gate.astype(np.float32), x
+
+
+@pytest.mark.parametrize("T,E,k,H,dt", PERM_CASES)
+def test_permute_bit_exact(abi, T, E, k, H, dt):
+    r, idx, gate, x = _perm_inputs(T, E, k, H, dt, T * 3 + E)
+    R = T * k
+    tdt = _tdt(dt)
+    X = dev(x, tdt)
+    xp = torch.empty(R, H, dtype=tdt, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    rmap = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    src = torch.empty(R, dtype=torch.int32, device="cuda")
+    wsb = abi.moe_permute_workspace_bytes(T, E, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    abi.moe_permute(X, _code(abi, dt), dev(idx, torch.int32), T, H, E, k, xp, counts, offsets,
+                    rmap, src, ws, wsb)
+    torch.cuda.synchronize()
+    rxp, rc, ro, rm, rs = oracle.permute(x, idx, E)
+    assert np.array_equal(host(counts), rc)
+    assert np.array_equal(host(offsets), ro)
+    assert np.array_equal(host(rmap), rm)
+    assert np.array_equal(host(src), rs)
+    assert np.array_equal(host(xp), rxp)          # a bit copy of bf16/fp32 values
+
+
+@pytest.mark.parametrize("T,E,k,H,dt", PERM_CASES)
+def test_combine_and_backward(abi, T, E, k, H, dt):
+    r, idx, gate, x = _perm_inputs(T, E, k, H, dt, T * 5 + E)
+    R = T * k
+    tdt = _tdt(dt)
+    _, _, _, rmap, _ = oracle.permute(x, idx, E)
+    yp = _store(r.standard_normal((R, H)), dt)
+    ys = _store(r.standard_normal((T, H)), dt)
+    dy = _store(r.standard_normal((T, H)), dt)
+    RM, G = dev(rmap, torch.int32), dev(gate, torch.float32)
+    YP, YS, DY = dev(yp, tdt), dev(ys, tdt), dev(dy, tdt)
+    code = _code(abi, dt)
+    tol = TOL[dt]
+    for with_shared in (False, True):
+        y = torch.empty(T, H, dtype=tdt, device="cuda")
+        abi.moe_unpermute_combine(YP, RM, G, YS if with_shared else None, code, T, H, k, y)
+        torch.cuda.synchronize()
+        ref = oracle.combine(yp, rmap, gate, ys if with_shared else None)
+        assert rel_err(host(y), ref) <= tol
+    dyp = torch.empty(R, H, dtype=tdt, device="cuda")
+    dgate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    abi.moe_unpermute_combine_bwd(DY, YP, RM, G, code, T, H, k, dyp, dgate)
+    torch.cuda.synchronize()
+    rdyp, rdg = oracle.combine_backward(dy, yp, rmap, gate)
+    assert rel_err(host(dyp), rdyp) <= tol
+    assert rel_err(host(dgate), rdg) <= 1e-5      # fp32 dot of storage values
+    # permute backward with two addends
+    dxp = _store(r.standard_normal((R, H)), dt)
+    a0 = _store(r.standard_normal((T, H)), dt)
+    a1 = _store(r.standard_normal((T, H)), dt)
+    dx = torch.empty(T, H, dtype=tdt, device="cuda")
+    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, dev(a0, tdt), dev(a1, tdt), dx)
+    torch.cuda.synchronize()
+    ref = oracle.permute_backward(dxp, rmap) + a0 + a1
+    assert rel_err(host(dx), ref) <= tol
+    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, None, None, dx)
+    torch.cuda.synchronize()
+    assert rel_err(host(dx), oracle.permute_backward(dxp, rmap)) <= tol
+
+
+def test_permute_empty_input(abi):
+    E = 16
+    counts = torch.full((E,), 7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
+    abi.moe_permute(None, abi.MOE_BF16, None, 0, 128, E, 2, None, counts, offsets, None, None,
+                    None, 0)
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------- router projection
+
+@pytest.mark.parametrize("T,H,E,dt", [(256, 128, 8, "f32"), (1000, 2048, 64, "bf16"),
+                                      (300, 7680, 256, "bf16")])
+def test_router_projection(abi, T, H, E, dt):
+    r = _rng(T + H)
+    x = _store(r.standard_normal((T, H)), dt)
+    wg = (r.standard_normal((H, E)) * 0.02).astype(np.float32)
+    bias = (r.standard_normal(E) * 0.5).astype(np.float32)
+    tdt = _tdt(dt)
+    X, WG, B = dev(x, tdt), dev(wg, torch.float32), dev(bias, torch.float32)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    abi.moe_router_logits(X, _code(abi, dt), WG, B, T, H, E, logits)
+    torch.cuda.synchronize()
+    assert rel_err(host(logits), oracle.router_logits(x, wg, bias)) <= 1e-5
+    dl = r.standard_normal((T, E)).astype(np.float32)
+    dx = torch.empty(T, H, dtype=tdt, device="cuda")
+    dwg = torch.empty(H, E, dtype=torch.float32, device="cuda")
+    db = torch.empty(E, dtype=torch.float32, device="cuda")
+    abi.moe_router_logits_bwd(dev(dl, torch.float32), X, _code(abi, dt), WG, T, H, E, dx, dwg, db)
+    torch.cuda.synchronize()
+    rdx, rdwg, rdb = oracle.router_backward(dl, x, wg)
+    assert rel_err(host(dx), rdx) <= TOL[dt]
+    assert rel_err(host(dwg), rdwg) <= 1e-5
+    assert rel_err(host(db), rdb) <= 1e-5
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+GMM_CASES = [
+    # counts per routed group, H, I, g0, G (None = all), shared rows, dtype
+    ([300, 0, 17, 1, 256, 64, 0, 513], 256, 192, 0, None, 0, "bf16"),
+    ([300, 0, 17, 1, 256, 64, 0, 513], 256, 192, 0, None, 0, "f32"),
+    ([5, 40, 0, 700, 3, 90], 512, 128, 2, 3, 200, "bf16"),
+    ([128, 64], 128, 64, 0, None, 77, "f32"),
+    ([0, 0, 0], 128, 64, 0, None, 0, "bf16"),
+    ([1000], 384, 320, 0, None, 0, "bf16"),
+    ([], 256, 128, 0, 0, 300, "bf16"),
+]
+
+
+@pytest.mark.parametrize("counts,H,I,g0,G,shT,dt", GMM_CASES)
+def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt):
+    r = _rng(sum(counts) + H + I + g0)
+    E = len(counts)
+    G = E - g0 if G is None else G
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    R = int(offsets[-1]) + 5                 # a few rows past the last group
+    tdt, code, tol = _tdt(dt), _code(abi, dt), TOL[dt]
+    xp = _store(r.standard_normal((R, H)), dt)
+    dyp = _store(r.standard_normal((R, H)), dt)
+    w13 = _store(r.standard_normal((max(G, 1), 2 * I, H)) * 0.05, dt)
+    w2 = _store(r.standard_normal((max(G, 1), H, I)) * 0.05, dt)
+    sx = _store(r.standard_normal((shT, H)), dt)
+    sdy = _store(r.standard_normal((shT, H)), dt)
+    sw13 = _store(r.standard_normal((2 * I, H)) * 0.05, dt)
+    sw2 = _store(r.standard_normal((H, I)) * 0.05, dt)
+
+    def z(*s):
+        return torch.zeros(*s, dtype=tdt, device="cuda")
+
+    OFF = dev(offsets if E else np.zeros(1), torch.int32)
+    XP, DYP, W13, W2 = dev(xp, tdt), dev(dyp, tdt), dev(w13, tdt), dev(w2, tdt)
+    h13, act, yp = z(R, 2 * I), z(R, I), z(R, H)
+    dh13, dxp = z(R, 2 * I), z(R, H)
+    dw13, dw2 = torch.full((max(G, 1), 2 * I, H), 9.0, dtype=tdt, device="cuda"), \
+        torch.full((max(G, 1), H, I), 9.0, dtype=tdt, device="cuda")
+    sh = None
+    if shT:
+        SX, SDY = dev(sx, tdt), dev(sdy, tdt)
+        shb = dict(x=SX, w13=dev(sw13, tdt), w2=dev(sw2, tdt), h13=z(shT, 2 * I), act=z(shT, I),
+                   y=z(shT, H), dy=SDY, dh13=z(shT, 2 * I), dx=z(shT, H), dw13=z(2 * I, H),
+                   dw2=z(H, I))
+        sh = abi.shared_expert(T=shT, **shb)
+    abi.moe_grouped_gemm_fwd(XP, OFF, g0, G, R, code, H, I, W13, W2, h13, act, yp, sh)
+    torch.cuda.synchronize()
+    ws = lambda g: w13[g]
+    rh13, ract, ryp = oracle.grouped_forward(xp, offsets, w13, w2, g0, G) if E else \
+        (np.zeros((R, 2 * I)), np.zeros((R, I)), np.zeros((R, H)))
+    assert rel_err(host(h13), rh13) <= tol
+    assert rel_err(host(act), ract) <= tol
+    assert rel_err(host(yp), ryp) <= tol
+    # backward dX / dW on the GPU's own saved activations
+    abi.moe_grouped_gemm_bwd_dx(DYP, OFF, g0, G, R, code, H, I, W13, W2, h13, dh13, dxp, sh)
+    abi.moe_grouped_gemm_bwd_dw(XP, act, DYP, dh13, OFF, g0, G, R, code, H, I, dw13, dw2, sh)
+    torch.cuda.synchronize()
+    if E:
+        rdh13, rdxp, rdw13, rdw2 = oracle.grouped_backward(xp, dyp, offsets, w13, w2, g0, G)
+        assert rel_err(host(dh13), rdh13) <= tol
+        assert rel_err(host(dxp), rdxp) <= tol
+        assert rel_err(host(dw13)[:G], rdw13) <= tol
+        assert rel_err(host(dw2)[:G], rdw2) <= tol
+        for g in range(G):                     # empty groups: exact zeros
+            if counts[g0 + g] == 0:
+                assert not host(dw13)[g].any() and not host(dw2)[g].any()
+    if shT:
+        rh, ra, ry = oracle.expert_forward(sx, sw13, sw2)
+        assert rel_err(host(shb["h13"]), rh) <= tol
+        assert rel_err(host(shb["y"]), ry) <= tol
+        rdh, rdx, rdw13s, rdw2s = oracle.expert_backward(sx, sw13, sw2, sdy)
+        assert rel_err(host(shb["dh13"]), rdh) <= tol
+        assert rel_err(host(shb["dx"]), rdx) <= tol
+        assert rel_err(host(shb["dw13"]), rdw13s) <= tol
+        assert rel_err(host(shb["dw2"]), rdw2s) <= tol
+    # rows outside the window are untouched
+    if E:
+        lo, hi = int(offsets[g0]), int(offsets[g0 + G])
+        for t in (yp, dxp, h13):
+            hv = host(t)
+            assert not hv[:lo].any() and not hv[hi:].any()
