@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE expert layer forward + backward on one MI355X.
+
+Workload: the Pangu-Ultra-shaped one-device share -- T = 8192 tokens (one
+8K sequence), hidden 7680, 256 routed experts with top-8 softmax gating and a
+Zipf(1.1) router bias; the grouped GEMM runs the 8 local experts (expert
+intermediate 2048, SwiGLU) plus one always-on shared expert (intermediate
+2048) on every token.  bf16 storage, fp32 accumulation, fp32 router.
+Inputs are seeded synthetic tensors (no dataset), resident in HBM before the
+timed region.
+
+A step is the whole path: router projection, route, permute, grouped GEMM
+forward (+ shared expert), unpermute/combine, combine backward, grouped GEMM
+dX and dW (+ shared expert), route backward, router backward, permute
+backward.  ``value`` is tokens per second over the timed steps.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/s on 1 GPU; GMM % MFMA peak; permute % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="pangu")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=4096,
+                   help="tokens in the oracle's timed sample")
+    return p.parse_args()
+
+
+CALLS = ["router_fwd", "route", "permute", "gmm_fwd", "combine", "combine_bwd", "gmm_bwd_dx",
+         "gmm_bwd_dw", "route_bwd", "router_bwd", "permute_bwd"]
+
+
+def algorithmic(cfg, rows_local):
+    """Algorithmic flops / bytes per call (routed rows only, no padding)."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    b = 2 if cfg.dtype == "bf16" else 4
+    rows = rows_local + (T if cfg.shared else 0)
+    gmm_flops = 6.0 * rows * H * I
+    n_experts = cfg.groups + (1 if cfg.shared else 0)
+    gmm_w_bytes = n_experts * 6.0 * H * I * b
+    out = {
+        "router_fwd": {"flops": 2.0 * T * H * E, "bytes": T * H * b + H * E * 4 + T * E * 4},
+        "route": {"bytes": 4.0 * T * E + 8.0 * T * k},
+        "permute": {"bytes": (1 + k) * T * H * b + 12.0 * T * k},
+        "gmm_fwd": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 3 * I) * b},
+        "combine": {"bytes": (k + 1) * T * H * b + 8.0 * T * k + (T * H * b if cfg.shared else 0)},
+        "combine_bwd": {"bytes": T * H * b + 2.0 * T * k * H * b + 12.0 * T * k},
+        "gmm_bwd_dx": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 4 * I) * b},
+        "gmm_bwd_dw": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 3 * I) * b},
+        "route_bwd": {"bytes": 8.0 * T * E + 12.0 * T * k},
+        "router_bwd": {"flops": 4.0 * T * H * E, "bytes": 2 * T * H * b + H * E * 4 + T * E * 4},
+        "permute_bwd": {"bytes": (k + 1) * T * H * b + 4.0 * T * k
+                        + (T * H * b if cfg.shared else 0) + (T * H * b if cfg.router else 0)},
+    }
+    return out
+
+
+def cpu_baseline(cfg_name, tokens):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    cfg = synth.get_config(cfg_name, T=tokens)
+    inp = synth.make_inputs(cfg)
+    acc = np.float32 if cfg.dtype == "bf16" else np.float64
+    t0 = time.perf_counter()
+    fwd = oracle.layer_forward(inp.x, cfg.k, cfg.E, inp.w13, inp.w2, wg=inp.wg, bias=inp.bias,
+                               logits=inp.logits, g0=cfg.g0, G=cfg.G, ws13=inp.ws13,
+                               ws2=inp.ws2, acc=acc)
+    oracle.layer_backward(fwd, inp.dy, inp.x, inp.w13, inp.w2, wg=inp.wg, g0=cfg.g0, G=cfg.G,
+                          ws13=inp.ws13, ws2=inp.ws2, acc=acc)
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg_name} layer fwd+bwd on the first {tokens} of the workload's "
+                      f"token count (same H/I/E/k, same seeds), numpy fp32 on bf16 inputs; "
+                      f"{dt:.1f} s", "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the layer here is one device's share; see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import make_layer
+
+    torch.cuda.set_device(0)
+    cfg = synth.get_config(args.config)
+    t_setup = time.time()
+    inp = synth.make_inputs(cfg)
+    L = make_layer(cfg, inp)
+    del inp
+    print(f"[bench] setup {time.time() - t_setup:.1f}s config={cfg.name}", file=sys.stderr,
+          flush=True)
+
+    calls = [c for c in CALLS if not (c.startswith("router") and not cfg.router)]
+    for _ in range(args.warmup):
+        L.step()
+    torch.cuda.synchronize()
+    rows = L.offsets.cpu().numpy()
+    rows_local = int(rows[cfg.g0 + cfg.groups] - rows[cfg.g0])
+
+    # timed region: K whole steps; events between calls on the working stream
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, c in enumerate(calls):
+            getattr(L, c)()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, c in enumerate(calls)}
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = cfg.T * args.steps / wall
+
+    alg = algorithmic(cfg, rows_local)
+    phases = {}
+    for c in calls:
+        ms = per_call[c]
+        d = {"ms": round(ms, 4)}
+        if "flops" in alg[c]:
+            tf = alg[c]["flops"] / (ms * 1e-3) / 1e12
+            d["tflops"] = round(tf, 1)
+            d["frac_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        gbs = alg[c]["bytes"] / (ms * 1e-3) / 1e9
+        d["gbs"] = round(gbs, 1)
+        d["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        phases[c] = d
+    dom = max((c for c in calls if c.startswith("gmm")), key=lambda c: per_call[c])
+    roof = {"kernel": f"moe_{'grouped_gemm_' + dom[4:]} (2 launches of gmm_kernel)",
+            "bound": "mfma", "achieved": phases[dom]["tflops"], "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": phases[dom]["frac_bf16_peak"], "traffic": None,
+            "flops_per_launch": alg[dom]["flops"], "ms_per_launch": round(per_call[dom], 4)}
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}; T={cfg.T} H={cfg.H} I={cfg.I} "
+                               f"E={cfg.E} top-{cfg.k}, grouped GEMM over experts "
+                               f"[{cfg.g0},{cfg.g0 + cfg.groups})"
+                               + (" + shared expert" if cfg.shared else "") + ", fwd+bwd",
+                   "tokens": cfg.T, "rows_local": rows_local, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "phases": phases,
+    }
+    del L
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, min(args.cpu_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 wave grid
   const int ng = a.G + a.shared;
 
   // ---- group table: clamped row ranges, then per-group tile prefix (M-var

@@ -36,7 +36,11 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * RT_BM, n0 = blockIdx.x * RT_BN;
   const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
-  float acc[4][4] = {};
+  // Each K step of 16 is summed on its own, then added to the running sum with
+  // Kahan compensation, so the rounding error does not grow with K (K is up
+  // to H = 7680 for the logits and T for dWg); it keeps near-equal logits in
+  // the right order.
+  float acc[4][4] = {}, comp[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += RT_BK) {
     // 64x16 A values and 16x64 B values, 4 each per thread
     for (int i = tid; i < RT_BM * RT_BK; i += 256) {
@@ -52,6 +56,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
       Bs[kk][nn] = (n < N && kq < K) ? B[kq * b_sk + n * b_sn] : 0.f;
     }
     __syncthreads();
+    float part[4][4] = {};
 #pragma unroll
     for (int kk = 0; kk < RT_BK; ++kk) {
       float a[4], b[4];
@@ -60,8 +65,17 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) part[i][j] = fmaf(a[i], b[j], part[i][j]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = part[i][j] - comp[i][j];
+        const float t = acc[i][j] + y;
+        comp[i][j] = (t - acc[i][j]) - y;
+        acc[i][j] = t;
+      }
     __syncthreads();
   }
 #pragma unroll

@@ -48,6 +48,12 @@ def check_layer(name, **overrides):
         ridx, _ = oracle.route(ref_logits, cfg.k)
         diff = np.any(host(L.idx) != ridx, axis=1)
         ties = near_tie_tokens(ref_logits, cfg.k)
+        if np.any(diff & ~ties):
+            s = -np.sort(-ref_logits.astype(np.float64), axis=1)
+            bad = np.where(diff & ~ties)[0]
+            gaps = s[bad, cfg.k - 1] - s[bad, cfg.k]
+            print("[layer] mismatched tokens", bad[:10], "gaps", gaps[:10],
+                  "max |logit err|", np.abs(lg[bad] - ref_logits[bad]).max(), flush=True)
         assert not np.any(diff & ~ties), "index mismatch away from a near tie"
         report["near_tie_tokens"] = int(ties.sum())
         report["mismatched_tokens"] = int(diff.sum())
