@@ -12,26 +12,31 @@
 // learns the counts ([MoE-ops] Host-Device section, Fig. 4).
 //
 // Tiling (the gfx950 counterpart of the staged GM -> L1 -> L0 pipeline and
-// the diagonal sub-block assignment of [MoE-ops], MatMul section, Fig. 2):
+// the diagonal sub-block assignment of [MoE-ops], MatMul section, Fig. 2, and
+// of the load / compute / store pipeline of [CANN-MoE] s2.2):
 //  - 256 x 256 output tile per 256-thread workgroup (4 wavefronts as 2 x 2,
-//    128 x 128 per wave = 4 x 4 MFMA 32x32 fragments, fp32 accumulators that
-//    live in the accumulation registers, one wavefront per SIMD);
-//  - K in steps of 128 bytes per row (64 bf16 / 32 fp32), double-buffered in
-//    LDS (2 x 64 KB): the next K step is fetched to registers while the MFMAs
-//    run on the current one, one barrier per step;
-//  - LDS rows of 128 bytes with an XOR swizzle of the 16-byte chunks, so the
-//    16-byte fragment reads and the transposed-block writes are spread over
-//    the banks without padding;
-//  - operands stored MN-major in HBM (weights in dX, both operands in dW) are
-//    read as 8x8 (bf16) / 4x4 (fp32) blocks and transposed in registers
-//    before the LDS write, so the MFMA always reads K-contiguous fragments;
-//  - all global accesses are raw buffer loads/stores whose range is the
-//    operand's valid rows: rows past a group's end read as zero and stray
-//    writes are dropped by the hardware;
+//    128 x 128 per wave = 4 x 4 MFMA 32x32 fragments, fp32 accumulators in
+//    the accumulation registers, one wavefront per SIMD);
+//  - K in steps of 64 bytes per row (32 bf16 / 16 fp32) through a ring of 4
+//    LDS stages (4 x 32 KB).  Tiles are copied HBM -> LDS by the buffer
+//    load-to-LDS path (no staging registers, no LDS store instructions) three
+//    steps ahead of the MFMAs, so three K steps of loads are in flight while
+//    one is multiplied;
+//  - an operand stored K-contiguous (activations, forward weights) sits in
+//    LDS as 256 rows of 64 bytes with the 16-byte chunks XOR-swizzled by row;
+//    an operand stored MN-contiguous (weights in dX, both operands in dW)
+//    sits as K rows of 256 elements, and the MFMA fragments are read with the
+//    gfx950 LDS transpose read (ds_read_b64_tr_b16), so no operand is ever
+//    transposed in registers or in HBM;
+//  - all global accesses are raw buffer accesses whose range is the operand's
+//    valid rows: rows past a group's end read as zero and stray writes are
+//    dropped by the hardware;
 //  - persistent grid of one workgroup per CU; tiles are ordered in bands of
 //    8 M-tiles per N-tile, and consecutive tile ids are kept on one XCD
 //    (workgroup ids are dealt round-robin over the 8 XCDs), so the
 //    workgroups sharing a weight panel share an L2.
+#include <type_traits>
+
 #include "validate.hpp"
 
 namespace {
@@ -39,10 +44,12 @@ namespace {
 constexpr int BM = 256, BN = 256, NT = 256;
 constexpr int WTM = 128, WTN = 128;  // wave tile
 constexpr int FM = 4, FN = 4;        // 32x32 fragments per wave tile
-constexpr int KCH = BM * 8 / NT;     // K-major 16-byte chunks per thread per operand
-constexpr int ROWB = 128;            // bytes per LDS tile row = one K step
-constexpr int TILE_BYTES = BM * ROWB;  // 32 KB per operand per stage
+constexpr int STAGES = 4;            // LDS ring depth (3 K steps in flight)
+constexpr int OPB = 16384;           // bytes of one operand tile in one stage
+constexpr int STAGE_BYTES = 2 * OPB;
+constexpr int DMA_PER_OP = OPB / 1024 / (NT / 64);   // 1 KB copies per wave per operand
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
+constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
 constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer range
 
 enum Mode { FWD1 = 0, FWD2 = 1, DX1 = 2, DX2 = 3, DW = 4 };
@@ -64,15 +71,59 @@ struct GmmArgs {
 
 template <typename T> struct Cfg;
 template <> struct Cfg<bf16_t> {
-  static constexpr int ES = 2, VEC = 8, BK = 64, KS = 4;  // 4 MFMA k-steps of 16
+  static constexpr int ES = 2, VEC = 8, BK = 32, KS = 2;   // 2 MFMA k-steps of 16
 };
 template <> struct Cfg<float> {
-  static constexpr int ES = 4, VEC = 4, BK = 32, KS = 16;  // 16 MFMA k-steps of 2
+  static constexpr int ES = 4, VEC = 4, BK = 16, KS = 8;   // 8 MFMA k-steps of 2
 };
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  const int swz = (row & 7) ^ ((row >> 3) & 7);
-  return row * ROWB + ((chunk ^ swz) << 4);
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_t;
+
+// K-major stage tile: 256 rows x 64 bytes; 16-byte chunk c of row r lives in
+// slot c ^ ((r >> 2) & 3), so 16 consecutive rows read at one chunk hit 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int kslot_off(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+// MN-major stage tile (bf16): 32 K rows x 512 bytes; 16-byte chunk c of row k
+// lives in slot c ^ (4 * (k & 3)), so the four rows of one transpose read
+// land in distinct bank groups.
+__device__ __forceinline__ int mslot_off_bf16(int k, int chunk) {
+  return k * 512 + ((chunk ^ ((k & 3) << 2)) << 4);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// Raw buffer descriptor as four SGPR words (range-checked, stride 0).
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return i32x4{uniform((int)(uint32_t)b), uniform((int)((b >> 32) & 0xffffu)), uniform((int)bytes),
+               MOE_RSRC_DW3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t*)p;
+}
+
+// One 1 KB HBM -> LDS copy: lane l's 16 bytes at voff + soff land at
+// lds + 16 l.  Issued as inline assembly so that the compiler does not guard
+// every later LDS read with a wait on all outstanding copies; the kernel
+// waits for exactly the copies it needs (wait_vm) before a barrier.
+__device__ __forceinline__ void dma16(const i32x4& rs, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(uniform((int)lds))
+               : "memory");
+}
+
+// Wait until at most n of this wave's buffer loads are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ f32x16 mfma_step(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -83,154 +134,150 @@ __device__ __forceinline__ f32x16 mfma_step(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// 8x8 bf16 block transpose: in[r] holds 8 values of row r (2 per dword);
-// out[c] holds column c's 8 values.
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) w[d] = __builtin_amdgcn_perm(in[2 * d + 1][c >> 1], in[2 * d][c >> 1], sel);
-    out[c] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) out[c] = u32x4{in[0][c], in[1][c], in[2][c], in[3][c]};
-}
-
 // Operand view: rsrc covers the valid bytes; element (mn, k) lives at
 //   K-major:  mn * ld + k        MN-major:  k * ld + mn      (elements)
 struct View {
-  __amdgpu_buffer_rsrc_t rs;
+  i32x4 rs;
   int ld;
   int mn_lim;   // mn >= mn_lim reads zero
 };
 
 __device__ __forceinline__ View make_view(const void* base, long long bytes, int ld, int mn_lim) {
   View v;
-  v.rs = make_rsrc(base, clamp_bytes(bytes));
+  v.rs = raw_rsrc(base, clamp_bytes(bytes));
   v.ld = ld;
   v.mn_lim = mn_lim;
   return v;
 }
 
-// ---------------------------------------------------------------- loaders
-// K-major tile: 256 rows x 8 chunks, KCH chunks per thread.
+// ---------------------------------------------------------------- HBM -> LDS
+// One operand tile of one K step is 16 copies of 1 KB, DMA_PER_OP per wave.
+// The per-lane byte offsets of a tile are fixed; a K step only moves the
+// uniform offset (k0 * ES for K-major, k0 * ld * ES for MN-major).
+//
+// K-major: copy q covers rows 16q..16q+15; lane l fills row 16q + l/4, slot l%4.
 template <typename T, bool SWIGLU>
-__device__ __forceinline__ void load_kmajor(const View& v, int mn0, int k0, int i0, int I,
-                                            u32x4 (&r)[KCH]) {
+__device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
+                                               uint32_t (&off)[DMA_PER_OP]) {
   constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int lin = i * NT + (int)threadIdx.x;
-    const int row = lin >> 3, ch = lin & 7;
+  for (int j = 0; j < DMA_PER_OP; ++j) {
+    const int q = wave * DMA_PER_OP + j;
+    const int row = q * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     int src;
     bool ok;
     if (SWIGLU) {
       // per wave column block of 128 rows: rows [128w, 128w+64) are gate rows
-      // i0+64w+c, rows [128w+64, 128w+128) the up rows I+i0+64w+c
-      const int w = row >> 7, q = row & 127;
-      const int c = w * 64 + (q & 63);
-      src = ((q >> 6) ? I : 0) + i0 + c;
-      ok = i0 + c < I;
+      // i0+64w+c, rows [128w+64, 128w+128) the up rows I+i0+64w+c (i0 = mn0)
+      const int w = row >> 7, r = row & 127;
+      const int c = w * 64 + (r & 63);
+      src = ((r >> 6) ? I : 0) + mn0 + c;
+      ok = mn0 + c < I;
     } else {
       src = mn0 + row;
       ok = src < v.mn_lim;
     }
-    const uint32_t off = ok ? (uint32_t)(((long long)src * v.ld + k0 + ch * VEC) * ES) : OOB;
-    r[i] = buf_load16(v.rs, off);
+    off[j] = ok ? (uint32_t)(((long long)src * v.ld + chunk * VEC) * ES) : OOB;
   }
 }
 
+// MN-major: bf16 copy q covers K rows 2q, 2q+1 (lane l: row 2q + l/32, slot
+// l%32); fp32 copy q covers K row q (lane l: slot l).
 template <typename T>
-__device__ __forceinline__ void store_kmajor(char* lds, const u32x4 (&r)[KCH]) {
+__device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
+                                                uint32_t (&off)[DMA_PER_OP]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int lin = i * NT + (int)threadIdx.x;
-    *(u32x4*)(lds + lds_off(lin >> 3, lin & 7)) = r[i];
+  for (int j = 0; j < DMA_PER_OP; ++j) {
+    const int q = wave * DMA_PER_OP + j;
+    int k, chunk;
+    if constexpr (sizeof(T) == 2) {
+      k = 2 * q + (lane >> 5);
+      chunk = (lane & 31) ^ ((k & 3) << 2);
+    } else {
+      k = q;
+      chunk = lane;
+    }
+    const int mn = mn0 + chunk * VEC;
+    off[j] = mn < v.mn_lim ? (uint32_t)(((long long)k * v.ld + mn) * ES) : OOB;
   }
 }
 
-// MN-major tile: blocks of VEC (k) x VEC (mn); block b: mn-vector b % (256/VEC),
-// k-vector b / (256/VEC).
-template <typename T>
-__device__ __forceinline__ void load_mnmajor(const View& v, int mn0, int k0, int blk,
-                                             u32x4 (&r)[Cfg<T>::VEC]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, NMV = BM / VEC;
-  const int mo = blk % NMV, ko = blk / NMV;
-  const int mn = mn0 + mo * VEC;
-  const bool ok = mn < v.mn_lim;
+__device__ __forceinline__ void issue_op(const View& v, const char* lds_op,
+                                         const uint32_t (&off)[DMA_PER_OP], int soff) {
+  const int wave = threadIdx.x >> 6;
+  const uint32_t base = lds_addr(lds_op) + wave * DMA_PER_OP * 1024;
 #pragma unroll
-  for (int rr = 0; rr < VEC; ++rr) {
-    const int k = k0 + ko * VEC + rr;
-    const uint32_t off = ok ? (uint32_t)(((long long)k * v.ld + mn) * ES) : OOB;
-    r[rr] = buf_load16(v.rs, off);
-  }
+  for (int j = 0; j < DMA_PER_OP; ++j) dma16(v.rs, base + j * 1024, off[j], soff);
 }
 
-template <typename T>
-__device__ __forceinline__ void store_mnmajor(char* lds, int blk, const u32x4 (&r)[Cfg<T>::VEC]) {
-  constexpr int VEC = Cfg<T>::VEC, NMV = BM / VEC;
-  const int mo = blk % NMV, ko = blk / NMV;
-  u32x4 t[VEC];
-  transpose_block(r, t);
-#pragma unroll
-  for (int c = 0; c < VEC; ++c) *(u32x4*)(lds + lds_off(mo * VEC + c, ko)) = t[c];
-}
-
-// ---------------------------------------------------------------- MFMA on one stage
-template <typename T>
-__device__ __forceinline__ void compute_stage(const char* la, const char* lb, int wm, int wn,
-                                              f32x16 (&acc)[FM][FN]) {
+// ---------------------------------------------------------------- LDS -> MFMA
+// Fragment f of a wave: 32 rows (M or N) starting at r0, K step ks.
+// bf16 lane l holds elements k = 16 ks + 8 (l/32) + 0..7 of row r0 + l%32.
+template <typename T, bool MN>
+__device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
   const int lane = threadIdx.x & 63;
-  const int r32 = lane & 31, hi = lane >> 5;
   if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
-      u32x4 a[FM], b[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-        a[f] = *(const u32x4*)(la + lds_off(wm * WTM + f * 32 + r32, ks * 2 + hi));
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        b[f] = *(const u32x4*)(lb + lds_off(wn * WTN + f * 32 + r32, ks * 2 + hi));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
+    if constexpr (!MN) {
+      return *(const u32x4*)(lds + kslot_off(r0 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+      // transpose read: in a group of 16 lanes, lane i points at row k0 + i/4,
+      // columns c0 + 4 (i%4) .. +3 and receives column c0 + i of rows k0..k0+3
+      const int g = lane >> 4, i = lane & 15;
+      const int c0 = r0 + (g & 1) * 16;
+      const int kb = ks * 16 + (g >> 1) * 8 + (i >> 2);
+      const int col = c0 + 4 * (i & 3);
+      const char* p0 = lds + mslot_off_bf16(kb, col >> 3) + (col & 7) * 2;
+      const char* p1 = lds + mslot_off_bf16(kb + 4, col >> 3) + (col & 7) * 2;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(p0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(p1));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2.x, l2.y, h2.x, h2.y};
     }
   } else {
-#pragma unroll
-    for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
-      const int k = ks * 2 + hi;
-      float a[FM], b[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-        a[f] = *(const float*)(la + lds_off(wm * WTM + f * 32 + r32, k >> 2) + (k & 3) * 4);
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        b[f] = *(const float*)(lb + lds_off(wn * WTN + f * 32 + r32, k >> 2) + (k & 3) * 4);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
+    const int k = ks * 2 + (lane >> 5);
+    const int r = r0 + (lane & 31);
+    if constexpr (!MN) {
+      return *(const float*)(lds + kslot_off(r, k >> 2) + (k & 3) * 4);
+    } else {
+      return *(const float*)(lds + k * 1024 + r * 4);
     }
   }
 }
+
+template <typename T, bool A_MN, bool B_MN>
+struct Frags {
+  decltype(read_frag<T, A_MN>(nullptr, 0, 0)) a[FM];
+  decltype(read_frag<T, B_MN>(nullptr, 0, 0)) b[FN];
+  __device__ __forceinline__ void load(const char* la, const char* lb, int wm, int wn, int ks) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) a[f] = read_frag<T, A_MN>(la, wm * WTM + f * 32, ks);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) b[f] = read_frag<T, B_MN>(lb, wn * WTN + f * 32, ks);
+  }
+  __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
+  }
+};
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- the kernel
 template <typename T, int MODE>
 __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, BK = Cfg<T>::BK;
+  constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
-  constexpr int NBLK = (BM / VEC) * (ROWB / 16);   // transposed blocks per operand tile
+  constexpr int DMA_PER_STEP = 2 * DMA_PER_OP;   // buffer loads per wave per K step
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  static_assert(BM * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue slice must fit the ring");
   __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
 
   const int tid = threadIdx.x;
@@ -350,8 +397,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       const void* wb = sh ? a.sW : (const void*)((const char*)a.W + (long long)g * a.w_gs * ES);
       const int wrows = (MODE == FWD1) ? 2 * a.I : (B_MN ? a.K : a.N);  // stored rows of W
       const int wcols = B_MN ? a.N : a.K;
-      va.mn_lim = rows;
-      vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, B_MN ? a.N : a.N);
+      vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, a.N);
     } else {
       const void* pb = sh ? a.sX : a.X;
       const void* qb = sh ? a.sW : a.W;
@@ -370,141 +416,191 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int KT = (kdim + BK - 1) / BK;
-    constexpr int BPT = NBLK / NT;   // transposed blocks per thread per operand
-    static_assert(BPT * VEC == 8 && KCH == 8, "staging is 8 chunks per operand");
-    u32x4 ra[8], rb[8];
-    auto fetch = [&](int kt) {
-      const int k0 = kt * BK;
-      if constexpr (!A_MN) {
-        load_kmajor<T, false>(va, m0, k0, 0, 0, ra);
-      } else {
-#pragma unroll
-        for (int b = 0; b < BPT; ++b)
-          load_mnmajor<T>(va, m0, k0, b * NT + tid, *(u32x4(*)[VEC]) & ra[b * VEC]);
-      }
-      if constexpr (!B_MN) {
-        load_kmajor<T, MODE == FWD1>(vb, n0, k0, n0, a.I, rb);
-      } else {
-#pragma unroll
-        for (int b = 0; b < BPT; ++b)
-          load_mnmajor<T>(vb, n0, k0, b * NT + tid, *(u32x4(*)[VEC]) & rb[b * VEC]);
-      }
+    uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
+    if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
+    else kmajor_offsets<T, false>(va, m0, 0, offa);
+    if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
+    else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
+    const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
+    const int sb = B_MN ? vb.ld * BK * ES : BK * ES;
+    auto issue = [&](int kt) {
+      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+      issue_op(va, st, offa, kt * sa);
+      issue_op(vb, st + OPB, offb, kt * sb);
     };
-    auto commit = [&](int stage) {
-      char* la = smem + stage * 2 * TILE_BYTES;
-      char* lb = la + TILE_BYTES;
-      if constexpr (!A_MN) {
-        store_kmajor<T>(la, ra);
-      } else {
-#pragma unroll
-        for (int b = 0; b < BPT; ++b)
-          store_mnmajor<T>(la, b * NT + tid, *(const u32x4(*)[VEC]) & ra[b * VEC]);
-      }
-      if constexpr (!B_MN) {
-        store_kmajor<T>(lb, rb);
-      } else {
-#pragma unroll
-        for (int b = 0; b < BPT; ++b)
-          store_mnmajor<T>(lb, b * NT + tid, *(const u32x4(*)[VEC]) & rb[b * VEC]);
-      }
-    };
+    auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
 
+    // every wave must be done reading the ring (previous tile) and its
+    // epilogue stores must have left before the ring is refilled
+    wait_vm<0>();
+    __syncthreads();
     if (KT > 0) {
-      fetch(0);
-      commit(0);
+      for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+      if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
+      else if (KT == 2) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
       __syncthreads();
-    }
-    for (int kt = 0; kt < KT; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < KT) fetch(kt + 1);
-      compute_stage<T>(smem + st * 2 * TILE_BYTES, smem + st * 2 * TILE_BYTES + TILE_BYTES, wm, wn,
-                       acc);
-      if (kt + 1 < KT) commit(st ^ 1);
-      __syncthreads();
+      Frags<T, A_MN, B_MN> cur, nxt;
+      cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
+          if (ks == Cfg<T>::KS - 1) {
+            // K step kt+1 has landed once at most one later step of this
+            // wave's copies is outstanding; the barrier extends that to all
+            // waves and retires every read of the stage refilled next
+            if (kt + 1 < KT) {
+              if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
+              else wait_vm<0>();
+              __syncthreads();
+              if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+              nxt.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
+            }
+          } else {
+            nxt.load(stage(kt), stage(kt) + OPB, wm, wn, ks + 1);
+          }
+          cur.mma(acc);
+          cur = nxt;
+        }
+      }
     }
 
-    // ---- epilogue
-    const int col = lane & 31;
-    const int rsub = (lane >> 5) * 4;
+    // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
+    // every HBM access is a 16-byte row chunk
+    __syncthreads();   // every wave is done with the ring
+    float* ep = (float*)smem;
+    auto put = [&](auto fn0c, auto&& value) {
+      // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + lane%32
+      // (fn0 is a compile-time constant so the accumulators stay in registers)
+      constexpr int slice_fn0 = decltype(fn0c)::value;
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * WTM + f * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int c = (wn * 64 + j * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
+            ep[row * EP_PITCH + c] = value(f, slice_fn0 + j, r);
+          }
+      __syncthreads();
+    };
+    auto take = [&](auto&& consume) {
+      // 256 rows x 16 chunks of 8 columns, 16 per thread
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int idx = it * NT + tid;
+        const int row = idx >> 4, cc = (idx & 15) * 8;
+        float v[8];
+        const int pc = cc ^ (((row >> 2) & 1) << 5);   // rows 4 apart sit 128 bytes apart
+        const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + pc);
+        const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + pc + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        consume(row, cc, v);
+      }
+      __syncthreads();
+    };
+    auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, const float* v) {
+      if constexpr (sizeof(T) == 2) {
+        buf_store16(rs, elem * 2u, pack16(v, T()));
+      } else {
+        buf_store16(rs, elem * 4u, pack16(v, T()));
+        buf_store16(rs, elem * 4u + 16u, pack16(v + 4, T()));
+      }
+    };
+    auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, float* v) {
+      if constexpr (sizeof(T) == 2) {
+        unpack16(buf_load16(rs, elem * 2u), v, T());
+      } else {
+        unpack16(buf_load16(rs, elem * 4u), v, T());
+        unpack16(buf_load16(rs, elem * 4u + 16u), v + 4, T());
+      }
+    };
     if constexpr (MODE == FWD1) {
+      // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + lane%32,
+      // fragments 2,3 the matching up columns; LDS column c is i = i0 + c
       void* hb = sh ? a.sC : a.C;
       void* ab = sh ? a.sC2 : a.C2;
       const __amdgpu_buffer_rsrc_t hr = make_rsrc((char*)hb + (long long)rows0 * a.ldc * ES,
                                                   clamp_bytes((long long)rows * a.ldc * ES));
       const __amdgpu_buffer_rsrc_t ar = make_rsrc((char*)ab + (long long)rows0 * a.ldc2 * ES,
                                                   clamp_bytes((long long)rows * a.ldc2 * ES));
-      // fragments 0,1 of a wave hold gate columns, 2,3 the matching up columns
+      using Z = std::integral_constant<int, 0>;
+      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
+      take([&](int row, int c, const float* v) {
+        if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + n0 + c), v);
+      });
+      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn + 2][r]; });
+      take([&](int row, int c, const float* v) {
+        if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
+      });
+      // act = silu(g) * u in place of the gate accumulators
 #pragma unroll
-      for (int fn = 0; fn < FN / 2; ++fn) {
-        const int i = n0 + wn * (WTN / 2) + fn * 32 + col;
-        if (i >= a.I) continue;
+      for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = wm * WTM + f * 32 + (r >> 2) * 8 + rsub + (r & 3);
-            if (lr < rows) {
-              const float gv = acc[f][fn][r], uv = acc[f][fn + FN / 2][r];
-              const float av = gv * sigmoidf_(gv) * uv;
-              buf_store_elem<T>(hr, (uint32_t)(lr * a.ldc + i), gv);
-              buf_store_elem<T>(hr, (uint32_t)(lr * a.ldc + a.I + i), uv);
-              buf_store_elem<T>(ar, (uint32_t)(lr * a.ldc2 + i), av);
-            }
-          }
-      }
-    } else if constexpr (MODE == DX1) {
-      const void* hb = sh ? a.sAux : a.aux;
-      void* db = sh ? a.sC : a.C;
-      const __amdgpu_buffer_rsrc_t hr = make_rsrc((const char*)hb + (long long)rows0 * a.ldaux * ES,
-                                                  clamp_bytes((long long)rows * a.ldaux * ES));
-      const __amdgpu_buffer_rsrc_t dr = make_rsrc((char*)db + (long long)rows0 * a.ldc * ES,
-                                                  clamp_bytes((long long)rows * a.ldc * ES));
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int i = n0 + wn * WTN + fn * 32 + col;
-        if (i >= a.I) continue;
-#pragma unroll
-        for (int f = 0; f < FM; ++f)
+        for (int fn = 0; fn < FN / 2; ++fn)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int lr = wm * WTM + f * 32 + (r >> 2) * 8 + rsub + (r & 3);
-            if (lr < rows) {
-              const float gv = buf_load_elem<T>(hr, (uint32_t)(lr * a.ldaux + i));
-              const float uv = buf_load_elem<T>(hr, (uint32_t)(lr * a.ldaux + a.I + i));
-              const float d = acc[f][fn][r];
-              const float s = sigmoidf_(gv);
-              buf_store_elem<T>(dr, (uint32_t)(lr * a.ldc + i), d * uv * s * (1.0f + gv * (1.0f - s)));
-              buf_store_elem<T>(dr, (uint32_t)(lr * a.ldc + a.I + i), d * gv * s);
-            }
+            const float gv = acc[f][fn][r];
+            acc[f][fn][r] = gv * sigmoidf_(gv) * acc[f][fn + 2][r];
           }
-      }
+      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
+      take([&](int row, int c, const float* v) {
+        if (row < rows && n0 + c < a.I) store8(ar, (uint32_t)(row * a.ldc2 + n0 + c), v);
+      });
     } else {
-      // plain store: FWD2 / DX2 rows of C, or DW: dW[g] (M x N)
-      void* cb;
-      long long cbytes;
-      int lim_m;
-      if constexpr (MODE == DW) {
-        cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * ES);
-        cbytes = (long long)a.M * a.ldc * ES;
-        lim_m = a.M;
-      } else {
-        cb = (char*)(sh ? a.sC : a.C) + (long long)rows0 * a.ldc * ES;
-        cbytes = (long long)rows * a.ldc * ES;
-        lim_m = rows;
-      }
-      const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, clamp_bytes(cbytes));
+      // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
+      auto slice = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        put(std::integral_constant<int, 2 * h>{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
+        if constexpr (MODE == DX1) {
+          const void* hb = sh ? a.sAux : a.aux;
+          void* db = sh ? a.sC : a.C;
+          const __amdgpu_buffer_rsrc_t hr = make_rsrc(
+              (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
+          const __amdgpu_buffer_rsrc_t dr = make_rsrc(
+              (char*)db + (long long)rows0 * a.ldc * ES, clamp_bytes((long long)rows * a.ldc * ES));
+          take([&](int row, int c, const float* d) {
+            const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+            if (row < rows && i < a.I) {
+              float gv[8], uv[8], dg[8], du[8];
+              load8(hr, (uint32_t)(row * a.ldaux + i), gv);
+              load8(hr, (uint32_t)(row * a.ldaux + a.I + i), uv);
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int n = n0 + wn * WTN + fn * 32 + col;
-        if (n >= a.N) continue;
-#pragma unroll
-        for (int f = 0; f < FM; ++f)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = m0 + wm * WTM + f * 32 + (r >> 2) * 8 + rsub + (r & 3);
-            if (lr < lim_m) buf_store_elem<T>(cr, (uint32_t)(lr * a.ldc + n), acc[f][fn][r]);
+              for (int e = 0; e < 8; ++e) {
+                const float sg = sigmoidf_(gv[e]);
+                dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+                du[e] = d[e] * gv[e] * sg;
+              }
+              store8(dr, (uint32_t)(row * a.ldc + i), dg);
+              store8(dr, (uint32_t)(row * a.ldc + a.I + i), du);
+            }
+          });
+        } else {
+          // plain store: FWD2 / DX2 rows of C, or DW: dW[g] (M x N)
+          void* cb;
+          long long cbytes;
+          int lim_m;
+          if constexpr (MODE == DW) {
+            cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * ES);
+            cbytes = (long long)a.M * a.ldc * ES;
+            lim_m = a.M;
+          } else {
+            cb = (char*)(sh ? a.sC : a.C) + (long long)rows0 * a.ldc * ES;
+            cbytes = (long long)rows * a.ldc * ES;
+            lim_m = rows;
           }
-      }
+          const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, clamp_bytes(cbytes));
+          take([&](int row, int c, const float* v) {
+            const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+            const int m = m0 + row;
+            if (m < lim_m && n < a.N) store8(cr, (uint32_t)(m * a.ldc + n), v);
+          });
+        }
+      };
+      slice(std::integral_constant<int, 0>{});
+      slice(std::integral_constant<int, 1>{});
     }
   }
 }
