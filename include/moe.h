@@ -75,18 +75,29 @@ int moe_abi_version(void);
  * Router projection, kept in fp32 ([CANN-MoE] s4.2):
  *   logits[T,E] = x[T,H] . Wg[H,E] + bias[E]     (bias nullable)
  * x has storage type dt and is widened to fp32; products accumulate in fp32.
+ * For bf16 x with H and T multiples of 256 and E a multiple of 64 the
+ * products run on the bf16 matrix cores: Wg is split into three bf16 parts
+ * (together exact to fp32), K is cut into 8 slices summed in fp64, and the
+ * result stays within a few fp32 ulps of the exact product.  That path needs
+ * a workspace of moe_router_workspace_bytes(T,H,E,dt) bytes (256-byte
+ * aligned, contents scratch); for other shapes the size is 0 and ws may be
+ * NULL.
  */
+size_t moe_router_workspace_bytes(int T, int H, int E, int dt);
 int moe_router_logits(const void* x, int dt, const float* wg, const float* bias,
-                      int T, int H, int E, float* logits, moe_stream_t stream);
+                      int T, int H, int E, float* logits, void* ws, size_t ws_bytes,
+                      moe_stream_t stream);
 
 /* Backward of moe_router_logits:
  *   dx[T,H]  = dlogits . Wg^T        (written, storage type dt)
  *   dwg[H,E] = x^T . dlogits         (written, fp32)
  *   dbias[E] = sum_t dlogits[t,:]    (written, fp32; nullable)
+ * Same workspace as the forward (bf16 dx uses the high bf16 part of each
+ * factor only: it is stored in bf16).
  */
 int moe_router_logits_bwd(const float* dlogits, const void* x, int dt, const float* wg,
                           int T, int H, int E, void* dx, float* dwg, float* dbias,
-                          moe_stream_t stream);
+                          void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------- routing
  * Softmax -> top-k -> selection ([CANN-MoE] s2.1), one token per wavefront:

@@ -46,8 +46,9 @@ _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (_I, []),
-    "moe_router_logits": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P]),
-    "moe_router_logits_bwd": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_router_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_router_logits": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_router_logits_bwd": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -115,14 +116,19 @@ def moe_abi_version() -> int:
     return _lib.moe_abi_version()
 
 
-def moe_router_logits(x, dt, wg, bias, T, H, E, logits, stream=None):
+def moe_router_workspace_bytes(T, H, E, dt) -> int:
+    return _lib.moe_router_workspace_bytes(T, H, E, dt)
+
+
+def moe_router_logits(x, dt, wg, bias, T, H, E, logits, ws=None, ws_bytes=0, stream=None):
     _call("moe_router_logits", addr(x), dt, addr(wg), addr(bias), T, H, E, addr(logits),
-          _stream(stream))
+          addr(ws), ws_bytes, _stream(stream))
 
 
-def moe_router_logits_bwd(dlogits, x, dt, wg, T, H, E, dx, dwg, dbias=None, stream=None):
+def moe_router_logits_bwd(dlogits, x, dt, wg, T, H, E, dx, dwg, dbias=None, ws=None, ws_bytes=0,
+                          stream=None):
     _call("moe_router_logits_bwd", addr(dlogits), addr(x), dt, addr(wg), T, H, E, addr(dx),
-          addr(dwg), addr(dbias), _stream(stream))
+          addr(dwg), addr(dbias), addr(ws), ws_bytes, _stream(stream))
 
 
 def moe_route(logits, T, E, k, idx, gate, stream=None):

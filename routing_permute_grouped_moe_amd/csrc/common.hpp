@@ -142,3 +142,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 int moe_fail(int status, const char* fmt, ...);
 int moe_check_launch(const char* what);
 int moe_cu_count();
+// router products on the bf16 MFMA path (gmm.hip)
+int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, int H, int E, int S,
+                       hipStream_t s);
+int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, int E,
+                      hipStream_t s);
+int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, int H, int E, int S,
+                       hipStream_t s);

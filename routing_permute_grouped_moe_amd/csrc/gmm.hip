@@ -67,6 +67,11 @@ struct GmmArgs {
   void* C2; int ldc2;                         // FWD1: act
   // shared expert operands (same layouts)
   const void* sX; const void* sW; void* sC; const void* sAux; void* sC2;
+  // dense groups: all G groups have rows [0, shT) and their own operands at
+  // X + g*x_gs, W + g*w_gs, C + g*c_gs (elements); no offsets table
+  int dense; long long x_gs;
+  int kwrap;     // > 0: the A operand's K index wraps with this period
+  int out_f32;   // plain-store epilogue writes fp32 whatever T is
 };
 
 template <typename T> struct Cfg;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   // modes) or the group order by descending row count (DW).
   for (int g = tid; g < ng; g += NT) {
     int lo, hi;
-    if (g < a.G) {
+    if (g < a.G && !a.dense) {
       lo = a.offsets[a.g0 + g];
       hi = a.offsets[a.g0 + g + 1];
       lo = lo < 0 ? 0 : (lo > a.R ? a.R : lo);
@@ -387,11 +392,13 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
     rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
     const bool sh = g >= a.G;
+    const long long xg = a.dense ? (long long)g * a.x_gs * ES : 0;   // dense group bases
+    const int arows = a.kwrap > 0 ? a.kwrap : kdim;   // A rows a DW tile can touch
 
     // ---- operand views
     View va, vb;
     if constexpr (MODE != DW) {
-      const void* xb = sh ? a.sX : a.X;
+      const void* xb = sh ? a.sX : (const void*)((const char*)a.X + xg);
       va = make_view((const char*)xb + (long long)rows0 * a.ldx * ES, (long long)rows * a.ldx * ES,
                      a.ldx, rows);
       const void* wb = sh ? a.sW : (const void*)((const char*)a.W + (long long)g * a.w_gs * ES);
@@ -399,9 +406,9 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       const int wcols = B_MN ? a.N : a.K;
       vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, a.N);
     } else {
-      const void* pb = sh ? a.sX : a.X;
-      const void* qb = sh ? a.sW : a.W;
-      va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)kdim * a.ldx * ES,
+      const void* pb = sh ? a.sX : (const void*)((const char*)a.X + xg);
+      const void* qb = sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)g * a.w_gs * ES : 0));
+      va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
                      a.ldx, a.M);
       vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES, (long long)kdim * a.ldw * ES,
                      a.ldw, a.N);
@@ -423,9 +430,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
     const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
     const int sb = B_MN ? vb.ld * BK * ES : BK * ES;
+    const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
     auto issue = [&](int kt) {
       const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-      issue_op(va, st, offa, kt * sa);
+      issue_op(va, st, offa, (kt % wrap_steps) * sa);
       issue_op(vb, st + OPB, offb, kt * sb);
     };
     auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
@@ -582,20 +590,31 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           void* cb;
           long long cbytes;
           int lim_m;
+          const int OS = a.out_f32 ? 4 : ES;   // bytes per output element
           if constexpr (MODE == DW) {
-            cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * ES);
-            cbytes = (long long)a.M * a.ldc * ES;
+            cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * OS);
+            cbytes = (long long)a.M * a.ldc * OS;
             lim_m = a.M;
           } else {
-            cb = (char*)(sh ? a.sC : a.C) + (long long)rows0 * a.ldc * ES;
-            cbytes = (long long)rows * a.ldc * ES;
+            cb = (char*)(sh ? a.sC : a.C) + (a.dense ? (long long)g * a.c_gs * OS : 0) +
+                 (long long)rows0 * a.ldc * OS;
+            cbytes = (long long)rows * a.ldc * OS;
             lim_m = rows;
           }
           const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, clamp_bytes(cbytes));
+          const bool f32out = a.out_f32;
           take([&](int row, int c, const float* v) {
             const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
             const int m = m0 + row;
-            if (m < lim_m && n < a.N) store8(cr, (uint32_t)(m * a.ldc + n), v);
+            if (m < lim_m && n < a.N) {
+              const uint32_t e = (uint32_t)(m * a.ldc + n);
+              if (f32out) {
+                buf_store16(cr, e * 4u, pack16(v, 0.0f));
+                buf_store16(cr, e * 4u + 16u, pack16(v + 4, 0.0f));
+              } else {
+                store8(cr, e, v);
+              }
+            }
           });
         }
       };
@@ -791,4 +810,44 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
   a.C = dw13; a.ldc = H; a.c_gs = 2LL * I * H;
   if (use_sh) { a.sX = sh->dh13; a.sW = sh->x; a.sC = sh->dw13; }
   return launch_dt<DW>(dt, a, s, fn);
+}
+
+// ---------------------------------------------------------------- router products
+// The fp32 router projection on the bf16 MFMA path (used for bf16 tokens):
+// the fp32 factor is split into three bf16 parts (hi + mid + lo carry all 24
+// mantissa bits), each part's product with the exact bf16 tokens is exact in
+// fp32, and the K range is cut into S slices whose fp32 partial sums are
+// added in fp64 by the caller, which keeps the result within a few fp32 ulps.
+
+int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, int H, int E, int S,
+                       hipStream_t s) {
+  GmmArgs a = {};
+  a.dense = 1; a.G = S; a.shT = T; a.R = T;
+  a.N = E; a.K = 3 * (H / S); a.kwrap = H / S;
+  a.X = x; a.ldx = H; a.x_gs = H / S;
+  a.W = wg3s; a.ldw = E; a.w_gs = 3LL * (H / S) * E;
+  a.C = partials; a.ldc = E; a.c_gs = (long long)T * E; a.out_f32 = 1;
+  return launch<bf16_t, DX2>(a, s, "moe_router_logits");
+}
+
+int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, int E,
+                      hipStream_t s) {
+  GmmArgs a = {};
+  a.dense = 1; a.G = 1; a.shT = T; a.R = T;
+  a.N = H; a.K = E;
+  a.X = dlb; a.ldx = E;
+  a.W = wgb; a.ldw = E;
+  a.C = dx; a.ldc = H;
+  return launch<bf16_t, FWD2>(a, s, "moe_router_logits_bwd(dx)");
+}
+
+int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, int H, int E, int S,
+                       hipStream_t s) {
+  GmmArgs a = {};
+  a.dense = 1; a.G = S; a.shT = 3 * (T / S); a.R = T;
+  a.M = H; a.N = E; a.kwrap = T / S;
+  a.X = x; a.ldx = H; a.x_gs = (long long)(T / S) * H;
+  a.W = dl3s; a.ldw = E; a.w_gs = 3LL * (T / S) * E;
+  a.C = partials; a.ldc = E; a.c_gs = (long long)H * E; a.out_f32 = 1;
+  return launch<bf16_t, DW>(a, s, "moe_router_logits_bwd(dwg)");
 }

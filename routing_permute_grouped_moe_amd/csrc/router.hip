@@ -1,6 +1,15 @@
 // Router projection in fp32 ([CANN-MoE] s4.2 keeps the router in FP32) and
-// its backward.  The three products are small next to the expert GEMMs
-// (N = E or K = E), so they use one strided fp32 tile kernel:
+// its backward.
+//
+// bf16 tokens (H a multiple of 256, T a multiple of 256, E a multiple of 64)
+// take the MFMA path: the fp32 operand (Wg, or dlogits for dWg) is split into
+// three bf16 parts hi + mid + lo that carry all of its 24 mantissa bits; a
+// product of a bf16 token value with each part is exact in fp32, the grouped
+// GEMM kernel sums them over S = 8 K slices with fp32 accumulation, and the
+// slices are added in fp64.  The input gradient dx only needs bf16 accuracy
+// (it is stored in bf16) and uses the hi parts alone.
+//
+// Other shapes use one strided fp32 tile kernel:
 //   C[m,n] = sum_k A(m,k) B(k,n) (+ bias[n])
 // A(m,k) = A[m*a_sm + k*a_sk] (storage type TA, widened to fp32),
 // B(k,n) = B[k*b_sk + n*b_sn] (fp32).  64x64 tile per 256-thread block,
@@ -120,6 +129,123 @@ static void launch_router_gemm(hipStream_t s, const TA* A, long long a_sm, long 
                      b_sn, bias, M, N, K, C, c_sm);
 }
 
+// ---------------------------------------------------------------- MFMA path helpers
+
+#define RT_SPLIT 8   // K slices of the router products
+
+static bool mfma_path(int dt, int T, int H, int E) {
+  return dt == MOE_BF16 && H % (RT_SPLIT * 32) == 0 && T % (RT_SPLIT * 32) == 0 && E % 64 == 0;
+}
+
+// three bf16 parts of an fp32 value: hi = bf16(v), mid = bf16(v - hi),
+// lo = bf16(v - hi - mid) (each difference is exact in fp32)
+__device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(h);
+  m = f32_to_bf16(r1);
+  l = f32_to_bf16(r1 - bf16_to_f32(m));
+}
+
+// Wg [H,E] -> wg3s [S][3][H/S][E] (K rows of slice s: hi, mid, lo parts of
+// rows s*H/S .. ) and wgb [H,E] = hi part.
+__global__ __launch_bounds__(256) void split_wg_kernel(const float* __restrict__ wg, int H, int E,
+                                                       bf16_t* __restrict__ wg3s,
+                                                       bf16_t* __restrict__ wgb) {
+  const long long n = (long long)H * E;
+  const int hs = H / RT_SPLIT;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int h = (int)(i / E), e = (int)(i % E);
+    uint32_t p0, p1, p2;
+    split3(wg[i], p0, p1, p2);
+    const int sl = h / hs, hl = h % hs;
+    const long long base = ((long long)sl * 3 * hs + hl) * E + e;
+    wg3s[base] = (bf16_t)p0;
+    wg3s[base + (long long)hs * E] = (bf16_t)p1;
+    wg3s[base + 2LL * hs * E] = (bf16_t)p2;
+    if (wgb) wgb[i] = (bf16_t)p0;
+  }
+}
+
+// dl [T,E] -> dl3s [S][3][T/S][E] and dlb [T,E] = hi part.
+__global__ __launch_bounds__(256) void split_dl_kernel(const float* __restrict__ dl, int T, int E,
+                                                       bf16_t* __restrict__ dl3s,
+                                                       bf16_t* __restrict__ dlb) {
+  const long long n = (long long)T * E;
+  const int ts = T / RT_SPLIT;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int t = (int)(i / E), e = (int)(i % E);
+    uint32_t p0, p1, p2;
+    split3(dl[i], p0, p1, p2);
+    const int sl = t / ts, tl = t % ts;
+    const long long base = ((long long)sl * 3 * ts + tl) * E + e;
+    dl3s[base] = (bf16_t)p0;
+    dl3s[base + (long long)ts * E] = (bf16_t)p1;
+    dl3s[base + 2LL * ts * E] = (bf16_t)p2;
+    dlb[i] = (bf16_t)p0;
+  }
+}
+
+// out[i] = (bias[i % E]) + sum_s part[s][i], summed in fp64 in slice order.
+__global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restrict__ part,
+                                                            long long n, int E,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ out) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    double acc = bias ? (double)bias[i % E] : 0.0;
+#pragma unroll
+    for (int s = 0; s < RT_SPLIT; ++s) acc += (double)part[s * n + i];
+    out[i] = (float)acc;
+  }
+}
+
+// dbias: per-chunk column sums (256 tokens per chunk), then a fixed-order sum.
+__global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ dl, int T,
+                                                          int E, float* __restrict__ part) {
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  const int c = blockIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  const int t1 = min(T, (c + 1) * 256);
+  for (int t = c * 256; t < t1; ++t) s += dl[(long long)t * E + e];
+  part[(long long)c * E + e] = s;
+}
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part,
+                                                           int nchunk, int E,
+                                                           float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  double s = 0.0;
+  for (int c = 0; c < nchunk; ++c) s += (double)part[(long long)c * E + e];
+  out[e] = (float)s;
+}
+
+static int grid_for(long long n) {
+  long long g = (n + 255) / 256;
+  return (int)(g < 4096 ? (g < 1 ? 1 : g) : 4096);
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// workspace layout (bytes), forward and backward use it separately
+struct RouterWs {
+  size_t wg3s, wgb, part, dl3s, dlb, colpart, total;
+};
+static RouterWs router_ws_layout(int T, int H, int E) {
+  RouterWs w = {};
+  const size_t he = (size_t)H * E, te = (size_t)T * E;
+  size_t o = 0;
+  w.wg3s = o; o += align256(3 * he * 2);
+  w.wgb = o; o += align256(he * 2);
+  w.part = o;
+  size_t part_bytes = (size_t)RT_SPLIT * (te > he ? te : he) * 4;
+  o += align256(part_bytes);
+  w.dl3s = o; o += align256(3 * te * 2);
+  w.dlb = o; o += align256(te * 2);
+  w.colpart = o; o += align256((size_t)((T + 255) / 256) * E * 4);
+  w.total = o;
+  return w;
+}
+
 static int router_checks(const char* fn, int dt, int T, int H, int E) {
   MOE_TRY(moe_need_dt(dt, fn));
   MOE_TRY(moe_need_nonneg(T, fn, "T"));
@@ -127,11 +253,18 @@ static int router_checks(const char* fn, int dt, int T, int H, int E) {
   MOE_TRY(moe_need_ek(E, 1, fn));
   MOE_TRY(moe_need_elems(T, H, moe_dt_bytes(dt), fn, "x"));
   MOE_TRY(moe_need_elems(T, E, 4, fn, "logits"));
+  MOE_TRY(moe_need_elems((long long)RT_SPLIT * T, E, 4, fn, "router partial sums"));
   return MOE_OK;
 }
 
+extern "C" size_t moe_router_workspace_bytes(int T, int H, int E, int dt) {
+  if (T <= 0 || H <= 0 || E <= 0 || !mfma_path(dt, T, H, E)) return 0;
+  return router_ws_layout(T, H, E).total;
+}
+
 extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const float* bias, int T,
-                                 int H, int E, float* logits, moe_stream_t stream) {
+                                 int H, int E, float* logits, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream) {
   const char* fn = "moe_router_logits";
   MOE_TRY(router_checks(fn, dt, T, H, E));
   if (T == 0) return MOE_OK;
@@ -140,6 +273,23 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
   MOE_TRY(moe_opt_ptr(bias, fn, "bias", 4));
   MOE_TRY(moe_need_ptr(logits, fn, "logits", 4));
   hipStream_t s = (hipStream_t)stream;
+  if (mfma_path(dt, T, H, E)) {
+    const size_t need = moe_router_workspace_bytes(T, H, E, dt);
+    MOE_TRY(moe_need_ptr(ws, fn, "ws", 256));
+    if (ws_bytes < need)
+      return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    const RouterWs L = router_ws_layout(T, H, E);
+    char* w = (char*)ws;
+    bf16_t* wg3s = (bf16_t*)(w + L.wg3s);
+    float* part = (float*)(w + L.part);
+    hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
+                       wg3s, (bf16_t*)nullptr);
+    MOE_TRY(moe_check_launch(fn));
+    MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, s));
+    hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s,
+                       (const float*)part, (long long)T * E, E, bias, logits);
+    return moe_check_launch(fn);
+  }
   if (dt == MOE_BF16)
     launch_router_gemm<bf16_t, float>(s, (const bf16_t*)x, H, 1, wg, E, 1, bias, T, E, H, logits, E);
   else
@@ -149,7 +299,7 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
 
 extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt, const float* wg,
                                      int T, int H, int E, void* dx, float* dwg, float* dbias,
-                                     moe_stream_t stream) {
+                                     void* ws, size_t ws_bytes, moe_stream_t stream) {
   const char* fn = "moe_router_logits_bwd";
   MOE_TRY(router_checks(fn, dt, T, H, E));
   MOE_TRY(moe_need_ptr(dwg, fn, "dwg", 4));
@@ -161,7 +311,7 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
                        dim3(256), 0, s, (const float*)nullptr, 0LL, 0LL, (const float*)nullptr, 0LL,
                        0LL, (const float*)nullptr, H, E, 0, dwg, (long long)E);
     if (dbias)
-      hipLaunchKernelGGL(colsum_kernel, dim3((E + MOE_WAVE - 1) / MOE_WAVE), dim3(1024), 0, s,
+      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 255) / 256), dim3(256), 0, s,
                          (const float*)nullptr, 0, E, dbias);
     return moe_check_launch(fn);
   }
@@ -169,6 +319,46 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
   MOE_TRY(moe_need_ptr(x, fn, "x"));
   MOE_TRY(moe_need_ptr(wg, fn, "wg", 4));
   MOE_TRY(moe_need_ptr(dx, fn, "dx"));
+  const bool mfma = mfma_path(dt, T, H, E);
+  RouterWs L = router_ws_layout(T, H, E);
+  if (mfma || dbias) {
+    const size_t need = mfma ? L.total : 0;
+    if (mfma) {
+      MOE_TRY(moe_need_ptr(ws, fn, "ws", 256));
+      if (ws_bytes < need)
+        return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
+                        need);
+    }
+  }
+  const int nchunk = (T + 255) / 256;
+  if (mfma) {
+    char* w = (char*)ws;
+    bf16_t* wg3s = (bf16_t*)(w + L.wg3s);
+    bf16_t* wgb = (bf16_t*)(w + L.wgb);
+    float* part = (float*)(w + L.part);
+    bf16_t* dl3s = (bf16_t*)(w + L.dl3s);
+    bf16_t* dlb = (bf16_t*)(w + L.dlb);
+    hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
+                       wg3s, wgb);
+    MOE_TRY(moe_check_launch(fn));
+    hipLaunchKernelGGL(split_dl_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s, dlogits,
+                       T, E, dl3s, dlb);
+    MOE_TRY(moe_check_launch(fn));
+    MOE_TRY(moe_gmm_router_dx(dlb, wgb, dx, T, H, E, s));
+    MOE_TRY(moe_gmm_router_dwg(x, dl3s, part, T, H, E, RT_SPLIT, s));
+    hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s,
+                       (const float*)part, (long long)H * E, E, (const float*)nullptr, dwg);
+    MOE_TRY(moe_check_launch(fn));
+    if (dbias) {
+      float* colpart = (float*)(w + L.colpart);
+      hipLaunchKernelGGL(colsum_part_kernel, dim3(nchunk, (E + 255) / 256), dim3(256), 0, s,
+                         dlogits, T, E, colpart);
+      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 255) / 256), dim3(256), 0, s,
+                         (const float*)colpart, nchunk, E, dbias);
+      MOE_TRY(moe_check_launch(fn));
+    }
+    return MOE_OK;
+  }
   // dx[T,H] = dlogits[T,E] . Wg^T : B(k=e, n=h) = Wg[h*E + e]
   if (dt == MOE_BF16)
     launch_router_gemm<float, bf16_t>(s, dlogits, E, 1, wg, 1, E, nullptr, T, H, E, (bf16_t*)dx, H);
@@ -184,6 +374,7 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
                                      E);
   MOE_TRY(moe_check_launch(fn));
   if (dbias) {
+    // small shapes: one fixed-order column sum per expert
     hipLaunchKernelGGL(colsum_kernel, dim3((E + MOE_WAVE - 1) / MOE_WAVE), dim3(1024), 0, s,
                        dlogits, T, E, dbias);
     MOE_TRY(moe_check_launch(fn));

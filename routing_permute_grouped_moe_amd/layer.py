@@ -78,6 +78,8 @@ class MoeLayer:
         self.src_token = e(R, d=i32)
         self.ws_bytes = abi.moe_permute_workspace_bytes(T, E, k)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.rws_bytes = abi.moe_router_workspace_bytes(T, H, E, self.dt) if s.router else 0
+        self.rws = torch.empty(max(self.rws_bytes, 256), dtype=torch.uint8, device=dev)
         self.h13 = e(R, 2 * I)
         self.act = e(R, I)
         self.yp = z(R, H)            # remote rows stay zero
@@ -118,7 +120,7 @@ class MoeLayer:
     def router_fwd(self, stream=None):
         s = self.s
         abi.moe_router_logits(self.x, self.dt, self.wg, self.bias, s.T, s.H, s.E, self.logits,
-                              stream)
+                              self.rws, self.rws_bytes, stream)
 
     def route(self, stream=None):
         s = self.s
@@ -168,7 +170,8 @@ class MoeLayer:
     def router_bwd(self, stream=None):
         s = self.s
         abi.moe_router_logits_bwd(self.dlogits, self.x, self.dt, self.wg, s.T, s.H, s.E,
-                                  self.dx_router, self.dwg, self.dbias, stream)
+                                  self.dx_router, self.dwg, self.dbias, self.rws, self.rws_bytes,
+                                  stream)
 
     def permute_bwd(self, stream=None):
         s = self.s

@@ -179,7 +179,8 @@ def test_permute_empty_input(abi):
 # ---------------------------------------------------------------- router projection
 
 @pytest.mark.parametrize("T,H,E,dt", [(256, 128, 8, "f32"), (1000, 2048, 64, "bf16"),
-                                      (300, 7680, 256, "bf16")])
+                                      (300, 7680, 256, "bf16"), (2048, 2048, 64, "bf16"),
+                                      (8192, 7680, 256, "bf16"), (512, 256, 128, "bf16")])
 def test_router_projection(abi, T, H, E, dt):
     r = _rng(T + H)
     x = _store(r.standard_normal((T, H)), dt)
@@ -188,14 +189,17 @@ def test_router_projection(abi, T, H, E, dt):
     tdt = _tdt(dt)
     X, WG, B = dev(x, tdt), dev(wg, torch.float32), dev(bias, torch.float32)
     logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
-    abi.moe_router_logits(X, _code(abi, dt), WG, B, T, H, E, logits)
+    wsb = abi.moe_router_workspace_bytes(T, H, E, _code(abi, dt))
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    abi.moe_router_logits(X, _code(abi, dt), WG, B, T, H, E, logits, ws, wsb)
     torch.cuda.synchronize()
     assert rel_err(host(logits), oracle.router_logits(x, wg, bias)) <= 1e-5
     dl = r.standard_normal((T, E)).astype(np.float32)
     dx = torch.empty(T, H, dtype=tdt, device="cuda")
     dwg = torch.empty(H, E, dtype=torch.float32, device="cuda")
     db = torch.empty(E, dtype=torch.float32, device="cuda")
-    abi.moe_router_logits_bwd(dev(dl, torch.float32), X, _code(abi, dt), WG, T, H, E, dx, dwg, db)
+    abi.moe_router_logits_bwd(dev(dl, torch.float32), X, _code(abi, dt), WG, T, H, E, dx, dwg, db,
+                              ws, wsb)
     torch.cuda.synchronize()
     rdx, rdwg, rdb = oracle.router_backward(dl, x, wg)
     assert rel_err(host(dx), rdx) <= TOL[dt]
