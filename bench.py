@@ -41,8 +41,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="pangu")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=4096,
+    p.add_argument("--cpu-tokens", type=int, default=8192,
                    help="tokens in the oracle's timed sample")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one device-to-device copy of this many MiB before the timed "
+                        "region (a known-size reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -75,8 +78,10 @@ def algorithmic(cfg, rows_local):
     return out
 
 
-def cpu_baseline(cfg_name, tokens):
-    """Time the CPU oracle (as it stands) on a bounded sample of the workload."""
+def cpu_baseline(cfg_name, tokens, min_seconds=10.0, max_reps=8):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload:
+    the layer fwd+bwd on ``tokens`` tokens, repeated until about
+    ``min_seconds`` of CPU work have been timed."""
     import numpy as np
 
     import oracle
@@ -84,21 +89,41 @@ def cpu_baseline(cfg_name, tokens):
     cfg = synth.get_config(cfg_name, T=tokens)
     inp = synth.make_inputs(cfg)
     acc = np.float32 if cfg.dtype == "bf16" else np.float64
-    t0 = time.perf_counter()
-    fwd = oracle.layer_forward(inp.x, cfg.k, cfg.E, inp.w13, inp.w2, wg=inp.wg, bias=inp.bias,
-                               logits=inp.logits, g0=cfg.g0, G=cfg.G, ws13=inp.ws13,
-                               ws2=inp.ws2, acc=acc)
-    oracle.layer_backward(fwd, inp.dy, inp.x, inp.w13, inp.w2, wg=inp.wg, g0=cfg.g0, G=cfg.G,
-                          ws13=inp.ws13, ws2=inp.ws2, acc=acc)
-    dt = time.perf_counter() - t0
+    reps, spent = 0, 0.0
+    while reps < max_reps and (reps == 0 or spent < min_seconds):
+        t0 = time.perf_counter()
+        fwd = oracle.layer_forward(inp.x, cfg.k, cfg.E, inp.w13, inp.w2, wg=inp.wg,
+                                   bias=inp.bias, logits=inp.logits, g0=cfg.g0, G=cfg.G,
+                                   ws13=inp.ws13, ws2=inp.ws2, acc=acc)
+        oracle.layer_backward(fwd, inp.dy, inp.x, inp.w13, inp.w2, wg=inp.wg, g0=cfg.g0,
+                              G=cfg.G, ws13=inp.ws13, ws2=inp.ws2, acc=acc)
+        spent += time.perf_counter() - t0
+        reps += 1
+        del fwd
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{cfg_name} layer fwd+bwd on the first {tokens} of the workload's "
-                      f"token count (same H/I/E/k, same seeds), numpy fp32 on bf16 inputs; "
-                      f"{dt:.1f} s", "seconds": dt, "cpu": platform.processor() or platform.machine()}
+    return {"value": tokens * reps / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg_name} layer fwd+bwd on {tokens} tokens (same H/I/E/k and seeds as "
+                      f"the workload), numpy fp32 on bf16 inputs, {reps} repetitions, "
+                      f"{spent:.1f} s", "seconds": spent,
+            "cpu": platform.processor() or platform.machine()}
+
+
+def measured_traffic(call):
+    """HBM bytes per launch of ``call`` from the committed rocprofv3 byte
+    counters, if they were taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_pangu.json")
+    try:
+        rec = json.load(open(path))["calls"][call]
+        src = os.path.join(ROOT, "routing_permute_grouped_moe_amd", "csrc", rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["hbm_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -125,6 +150,13 @@ def main():
           flush=True)
 
     calls = [c for c in CALLS if not (c.startswith("router") and not cfg.router)]
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         L.step()
     torch.cuda.synchronize()
@@ -164,10 +196,14 @@ def main():
         d["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
         phases[c] = d
     dom = max((c for c in calls if c.startswith("gmm")), key=lambda c: per_call[c])
-    roof = {"kernel": f"moe_{'grouped_gemm_' + dom[4:]} (2 launches of gmm_kernel)",
+    dom_call = "moe_grouped_gemm_" + dom[4:]
+    traffic = measured_traffic(dom_call) if cfg.name == "pangu" else None
+    roof = {"kernel": f"{dom_call} (one call = 2 launches of gmm_kernel)",
             "bound": "mfma", "achieved": phases[dom]["tflops"], "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": phases[dom]["frac_bf16_peak"], "traffic": None,
-            "flops_per_launch": alg[dom]["flops"], "ms_per_launch": round(per_call[dom], 4)}
+            "unit": "TFLOP/s", "frac": phases[dom]["frac_bf16_peak"],
+            "traffic": round(traffic) if traffic else None,
+            "flops_per_launch": alg[dom]["flops"], "ms_per_launch": round(per_call[dom], 4),
+            "algorithmic_bytes": alg[dom]["bytes"]}
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
