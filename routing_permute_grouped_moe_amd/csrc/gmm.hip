@@ -253,6 +253,11 @@ __device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
   }
 }
 
+// The MFMA takes the B fragment as its first operand, so accumulator register
+// r of fragment (i, j) holds C[m][n] with m = 32 i + lane%32 and
+// n = 32 j + 8 (r/4) + 4 (lane/32) + r%4: every lane owns runs of four
+// consecutive output columns, which the epilogue writes to LDS as one
+// 16-byte store.
 template <typename T, bool A_MN, bool B_MN>
 struct Frags {
   decltype(read_frag<T, A_MN>(nullptr, 0, 0)) a[FM];
@@ -267,7 +272,7 @@ struct Frags {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step(b[j], a[i], acc[i][j]);
   }
 };
 
@@ -448,27 +453,47 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       else if (KT == 2) wait_vm<DMA_PER_STEP>();
       else wait_vm<0>();
       __syncthreads();
-      Frags<T, A_MN, B_MN> cur, nxt;
-      cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
-          if (ks == Cfg<T>::KS - 1) {
+      if constexpr (Cfg<T>::KS == 2) {
+        // two fragment sets in ping-pong: the k-step 1 fragments load while
+        // k-step 0 multiplies, and the next stage's k-step 0 fragments load
+        // (after the barrier) while k-step 1 multiplies
+        Frags<T, A_MN, B_MN> f0, f1;
+        f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
+        for (int kt = 0; kt < KT; ++kt) {
+          f1.load(stage(kt), stage(kt) + OPB, wm, wn, 1);
+          f0.mma(acc);
+          if (kt + 1 < KT) {
             // K step kt+1 has landed once at most one later step of this
             // wave's copies is outstanding; the barrier extends that to all
             // waves and retires every read of the stage refilled next
-            if (kt + 1 < KT) {
-              if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
-              else wait_vm<0>();
-              __syncthreads();
-              if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-              nxt.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
-            }
-          } else {
-            nxt.load(stage(kt), stage(kt) + OPB, wm, wn, ks + 1);
+            if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
+            else wait_vm<0>();
+            __syncthreads();
+            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+            f0.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
           }
-          cur.mma(acc);
-          cur = nxt;
+          f1.mma(acc);
+        }
+      } else {
+        Frags<T, A_MN, B_MN> cur, nxt;
+        cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+          for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
+            if (ks == Cfg<T>::KS - 1) {
+              if (kt + 1 < KT) {
+                if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
+                else wait_vm<0>();
+                __syncthreads();
+                if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+                nxt.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
+              }
+            } else {
+              nxt.load(stage(kt), stage(kt) + OPB, wm, wn, ks + 1);
+            }
+            cur.mma(acc);
+            cur = nxt;
+          }
         }
       }
     }
@@ -478,18 +503,26 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     __syncthreads();   // every wave is done with the ring
     float* ep = (float*)smem;
     auto put = [&](auto fn0c, auto&& value) {
-      // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + lane%32
-      // (fn0 is a compile-time constant so the accumulators stay in registers)
+      // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
+      // (fn0 is a compile-time constant so the accumulators stay in registers);
+      // 16-byte granule g of row m sits at g ^ (m % 32), so the 32 rows of a
+      // store and the 16 chunks of a row read all hit distinct banks
       constexpr int slice_fn0 = decltype(fn0c)::value;
+      const int m = lane & 31;
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * WTM + f * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int c = (wn * 64 + j * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
-            ep[row * EP_PITCH + c] = value(f, slice_fn0 + j, r);
+          for (int rq = 0; rq < 4; ++rq) {
+            const int row = wm * WTM + f * 32 + m;
+            const int g = (wn * 64 + j * 32 + rq * 8 + (lane >> 5) * 4) >> 2;
+            f32x4 v;
+            v.x = value(f, slice_fn0 + j, rq * 4 + 0);
+            v.y = value(f, slice_fn0 + j, rq * 4 + 1);
+            v.z = value(f, slice_fn0 + j, rq * 4 + 2);
+            v.w = value(f, slice_fn0 + j, rq * 4 + 3);
+            *(f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2)) = v;
           }
       __syncthreads();
     };
@@ -499,10 +532,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       for (int it = 0; it < 16; ++it) {
         const int idx = it * NT + tid;
         const int row = idx >> 4, cc = (idx & 15) * 8;
+        const int sw = row & 31;
         float v[8];
-        const int pc = cc ^ (((row >> 2) & 1) << 5);   // rows 4 apart sit 128 bytes apart
-        const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + pc);
-        const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + pc + 4);
+        const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
+        const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
         v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
         v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
         consume(row, cc, v);
