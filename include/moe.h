@@ -169,7 +169,16 @@ int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row
  * not touched (remote experts).  An optional shared expert runs on its own
  * T rows in the same launch (a dense group with its own weights).
  * Arithmetic: dt products, fp32 accumulation; outputs stored as dt.
+ *
+ * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes, 256-byte
+ * aligned, contents scratch.  With it the K steps of all tiles are spread
+ * evenly over the workgroups and a tile cut between two of them is finished
+ * by the last to arrive, which adds the fp32 partial tiles in a fixed order
+ * (results stay bitwise reproducible).  With ws == NULL every tile is
+ * computed whole by one workgroup (same results up to fp32 summation order).
+ * Calls that share one workspace must not run concurrently.
  */
+size_t moe_gmm_workspace_bytes(void);
 typedef struct moe_shared_expert {
   int T;             /* rows of the shared expert (tokens) */
   const void* x;     /* [T,H]  input rows (forward, dW) */
@@ -192,7 +201,7 @@ typedef struct moe_shared_expert {
 int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
                          int dt, int H, int I, const void* w13, const void* w2,
                          void* h13, void* act, void* yp, const moe_shared_expert* shared,
-                         moe_stream_t stream);
+                         void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Backward dX ([Pangu-QA]: dX is computed apart from dW):
  *   dact = dyp . w2[e];  g = h13[:, :I], u = h13[:, I:], s = sigmoid(g)
@@ -202,7 +211,8 @@ int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, 
 int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G, int R,
                             int dt, int H, int I, const void* w13, const void* w2,
                             const void* h13, void* dh13, void* dxp,
-                            const moe_shared_expert* shared, moe_stream_t stream);
+                            const moe_shared_expert* shared, void* ws, size_t ws_bytes,
+                            moe_stream_t stream);
 
 /* Backward dW, contraction over each group's rows (K = its row count):
  *   dw2[e]  = dyp_e^T . act_e     ([G,H,I])
@@ -211,7 +221,7 @@ int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int
 int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp, const void* dh13,
                             const int32_t* offsets, int g0, int G, int R, int dt, int H, int I,
                             void* dw13, void* dw2, const moe_shared_expert* shared,
-                            moe_stream_t stream);
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -56,12 +56,13 @@ _SIGS = {
     "moe_permute_bwd": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_unpermute_combine_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_gmm_workspace_bytes": (_SZ, []),
     "moe_grouped_gemm_fwd": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
-                                  ctypes.POINTER(SharedExpert), _P]),
+                                  ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
     "moe_grouped_gemm_bwd_dx": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
-                                     ctypes.POINTER(SharedExpert), _P]),
+                                     ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
     "moe_grouped_gemm_bwd_dw": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
-                                     ctypes.POINTER(SharedExpert), _P]),
+                                     ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -177,19 +178,26 @@ def _sh(sh):
     return ctypes.byref(sh) if sh is not None else None
 
 
+def moe_gmm_workspace_bytes() -> int:
+    return _lib.moe_gmm_workspace_bytes()
+
+
 def moe_grouped_gemm_fwd(xp, offsets, g0, G, R, dt, H, I, w13, w2, h13, act, yp, shared=None,
-                         stream=None):
+                         ws=None, ws_bytes=0, stream=None):
     _call("moe_grouped_gemm_fwd", addr(xp), addr(offsets), g0, G, R, dt, H, I, addr(w13),
-          addr(w2), addr(h13), addr(act), addr(yp), _sh(shared), _stream(stream))
+          addr(w2), addr(h13), addr(act), addr(yp), _sh(shared), addr(ws), ws_bytes,
+          _stream(stream))
 
 
 def moe_grouped_gemm_bwd_dx(dyp, offsets, g0, G, R, dt, H, I, w13, w2, h13, dh13, dxp,
-                            shared=None, stream=None):
+                            shared=None, ws=None, ws_bytes=0, stream=None):
     _call("moe_grouped_gemm_bwd_dx", addr(dyp), addr(offsets), g0, G, R, dt, H, I, addr(w13),
-          addr(w2), addr(h13), addr(dh13), addr(dxp), _sh(shared), _stream(stream))
+          addr(w2), addr(h13), addr(dh13), addr(dxp), _sh(shared), addr(ws), ws_bytes,
+          _stream(stream))
 
 
 def moe_grouped_gemm_bwd_dw(xp, act, dyp, dh13, offsets, g0, G, R, dt, H, I, dw13, dw2,
-                            shared=None, stream=None):
+                            shared=None, ws=None, ws_bytes=0, stream=None):
     _call("moe_grouped_gemm_bwd_dw", addr(xp), addr(act), addr(dyp), addr(dh13), addr(offsets),
-          g0, G, R, dt, H, I, addr(dw13), addr(dw2), _sh(shared), _stream(stream))
+          g0, G, R, dt, H, I, addr(dw13), addr(dw2), _sh(shared), addr(ws), ws_bytes,
+          _stream(stream))

@@ -136,6 +136,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform(long long v) {
+  const unsigned long long u = (unsigned long long)v;
+  return (long long)(((unsigned long long)(uint32_t)uniform((int)(uint32_t)(u >> 32)) << 32) |
+                     (uint32_t)uniform((int)(uint32_t)u));
+}
 
 // ---------------------------------------------------------------- host helpers
 // (defined in api.cpp)
@@ -143,9 +148,11 @@ int moe_fail(int status, const char* fmt, ...);
 int moe_check_launch(const char* what);
 int moe_cu_count();
 // router products on the bf16 MFMA path (gmm.hip)
+// (split_ws: the grouped GEMM's split-tile workspace, moe_gmm_split_ws_bytes())
+size_t moe_gmm_split_ws_bytes();
 int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, int H, int E, int S,
-                       hipStream_t s);
+                       void* split_ws, hipStream_t s);
 int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, int E,
-                      hipStream_t s);
+                      void* split_ws, hipStream_t s);
 int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, int H, int E, int S,
-                       hipStream_t s);
+                       void* split_ws, hipStream_t s);

@@ -51,6 +51,7 @@ constexpr int DMA_PER_OP = OPB / 1024 / (NT / 64);   // 1 KB copies per wave per
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
 constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
 constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer range
+constexpr int CPOL_SYS = 1 | 16;       // cache policy sc0 | sc1: system-coherent access
 
 enum Mode { FWD1 = 0, FWD2 = 1, DX1 = 2, DX2 = 3, DW = 4 };
 
@@ -72,6 +73,9 @@ struct GmmArgs {
   int dense; long long x_gs;
   int kwrap;     // > 0: the A operand's K index wraps with this period
   int out_f32;   // plain-store epilogue writes fp32 whatever T is
+  // split-tile workspace (NULL: every tile is computed whole by one workgroup)
+  int* cnt;      // one arrival counter per workgroup, zero on entry
+  float* part;   // 2 partial tiles (256 x 256 fp32) per workgroup
 };
 
 template <typename T> struct Cfg;
@@ -268,6 +272,12 @@ struct Frags {
 #pragma unroll
     for (int f = 0; f < FN; ++f) b[f] = read_frag<T, B_MN>(lb, wn * WTN + f * 32, ks);
   }
+  // fragment q of a load: q < FM is A fragment q, else B fragment q - FM
+  __device__ __forceinline__ void load1(const char* la, const char* lb, int wm, int wn, int ks,
+                                        int q) {
+    if (q < FM) a[q] = read_frag<T, A_MN>(la, wm * WTM + q * 32, ks);
+    else b[q - FM] = read_frag<T, B_MN>(lb, wn * WTN + (q - FM) * 32, ks);
+  }
   __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -289,6 +299,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
   static_assert(BM * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue slice must fit the ring");
   __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
+  __shared__ int g_kp[MOE_MAX_E + 2];   // DW: K steps before each group in work order
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -352,16 +364,80 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     MBt = (a.M + BM - 1) / BM;
     NBt = (a.N + BN - 1) / BN;
     total = ng * MBt * NBt;
+    // work of a group = its tiles x max(1, K steps) (an empty group still
+    // owns tiles that must be written with zeros)
+    if (wave == 0) {
+      const int per = (ng + 63) / 64;
+      const int b0 = lane * per, b1 = min(ng, b0 + per);
+      auto work = [&](int p) {
+        const int g = g_pre[p];
+        return MBt * NBt * max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
+      };
+      int s = 0;
+      for (int p = b0; p < b1; ++p) s += work(p);
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      int run = incl - s;
+      for (int p = b0; p < b1; ++p) {
+        g_kp[p] = run;
+        run += work(p);
+      }
+      if (lane == 63) g_kp[ng] = incl;
+    }
+    __syncthreads();
   }
 
-  // ---- persistent loop, XCD-aware workgroup numbering
+  // ---- persistent loop, XCD-aware workgroup numbering.  Whole tiles are
+  // dealt round-robin, so the workgroups in flight work on neighbouring tiles
+  // and share their operand panels in L2.  With a workspace, the tiles of the
+  // last one-to-two rounds (which would leave part of the chip idle) are
+  // instead cut along K: their K steps form one sequence split into equal
+  // contiguous ranges, one per workgroup; a tile cut by a range boundary is
+  // finished by the last of its workgroups to arrive, which adds the fp32
+  // partial tiles in workgroup order (deterministic) and runs the epilogue.
   const int nwg = gridDim.x;
   const int bid = blockIdx.x;
   const int L = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-
-  for (int tile = L; tile < total; tile += nwg) {
-    int g, m0, n0, rows0 = 0, rows = 0, kdim;
+  const int KTm = (a.K + BK - 1) / BK;   // K steps of an M-var tile
+  const int per = MBt * NBt;             // DW: tiles of one group
+  // first K step of tile t in the sequence of all tiles' K steps
+  auto kstart = [&](int t) -> long long {
     if constexpr (MODE != DW) {
+      return (long long)t * KTm;
+    } else {
+      if (t >= total) return g_kp[ng];
+      const int p = t / per;
+      const int gg = g_pre[p];
+      return g_kp[p] + (long long)(t % per) * max(1, (g_hi[gg] - g_lo[gg] + BK - 1) / BK);
+    }
+  };
+  const int rounds = total / nwg;
+  const int dp_tiles = (a.part != nullptr && total % nwg != 0) ? max(0, rounds - 1) * nwg : total;
+  const long long k0 = uniform(kstart(dp_tiles));
+  const long long W = uniform(kstart(total)) - k0;   // K steps of the cut region
+  // every sharing workgroup gets at least one K step (no empty ranges, so
+  // every workgroup counted on a cut tile does arrive)
+  const int nsh = (int)min((long long)nwg, W);
+  const bool active = L < nsh;
+  const long long r_beg = active ? k0 + W * L / nsh : 0;
+  const long long r_end = active ? k0 + W * (L + 1) / nsh : 0;
+  auto wg_of = [&](long long k) { return (int)(((k - k0 + 1) * nsh - 1) / W); };
+
+  long long cur = r_beg;
+  int rr_tile = L;
+  while (rr_tile < dp_tiles || cur < r_end) {
+    const bool split = rr_tile >= dp_tiles;
+    // ---- locate the round-robin tile or the tile holding K step cur
+    int tile, g, m0, n0, rows0 = 0, rows = 0, kdim, KTe;
+    long long t_start;
+    if constexpr (MODE != DW) {
+      tile = split ? (int)(cur / KTm) : rr_tile;
+      KTe = KTm;
+      t_start = (long long)tile * KTm;
       const int MT = g_pre[ng];
       const int band = GM_BAND * NBt;
       const int sup = tile / band, within = tile % band;
@@ -382,9 +458,26 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       n0 = nbi * ((MODE == FWD1) ? BN / 2 : BN);
       kdim = a.K;
     } else {
-      const int per = MBt * NBt;
-      g = g_pre[tile / per];
-      const int local = tile % per;
+      int p, local;
+      if (split) {
+        int lo = 0, hi = ng - 1;   // last work position with g_kp[p] <= cur
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (g_kp[mid] <= cur) lo = mid; else hi = mid - 1;
+        }
+        p = lo;
+        g = g_pre[p];
+        KTe = max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
+        local = (int)((cur - g_kp[p]) / KTe);
+        t_start = g_kp[p] + (long long)local * KTe;
+      } else {
+        p = rr_tile / per;
+        local = rr_tile % per;
+        g = g_pre[p];
+        KTe = max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
+        t_start = 0;
+      }
+      tile = p * per + local;
       const int band = GM_BAND * NBt;
       const int sup = local / band, within = local % band;
       const int first = sup * GM_BAND;
@@ -394,6 +487,12 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       rows0 = g_lo[g];
       kdim = g_hi[g] - g_lo[g];
     }
+    // K steps [s0, s1) of this tile belong to this workgroup
+    const int s0 = split ? (int)(cur - t_start) : 0;
+    const int s1 = split ? (int)min((long long)KTe, r_end - t_start) : KTe;
+    const bool whole = (s0 == 0 && s1 == KTe);
+    if (split) cur = t_start + s1; else rr_tile += nwg;
+    t_start = uniform(t_start); KTe = uniform(KTe);
     g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
     rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
     const bool sh = g >= a.G;
@@ -427,7 +526,9 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int KT = (kdim + BK - 1) / BK;
+    const int KTr = (kdim + BK - 1) / BK;            // K steps with data
+    const int kb = min(s0, KTr), ke = min(s1, KTr);  // this workgroup's steps
+    const int KT = ke - kb;
     uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
     if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
     else kmajor_offsets<T, false>(va, m0, 0, offa);
@@ -436,10 +537,29 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
     const int sb = B_MN ? vb.ld * BK * ES : BK * ES;
     const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
-    auto issue = [&](int kt) {
+    auto issue = [&](int kt) {   // kt counts from kb
       const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-      issue_op(va, st, offa, (kt % wrap_steps) * sa);
-      issue_op(vb, st + OPB, offb, kt * sb);
+      const int kg = kb + kt;
+      issue_op(va, st, offa, (kg % wrap_steps) * sa);
+      issue_op(vb, st + OPB, offb, kg * sb);
+    };
+    // copy j of K step kt (j < DMA_PER_OP: operand A, else B); a step past the
+    // last one copies through an empty descriptor, which moves no HBM bytes
+    // and only writes zeros into a stage nobody reads
+    const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
+    const uint32_t lds_w = lds_addr(smem) + (threadIdx.x >> 6) * DMA_PER_OP * 1024;
+    // (the A step index wraps for dW tiles that re-read a short operand;
+    // ka_next tracks (kb + kt) % wrap_steps of the next step to issue)
+    int ka_next = kb % wrap_steps;
+    auto issue1 = [&](int kt, int j) {
+      const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+      const bool live = kt < KT;
+      if (j < DMA_PER_OP)
+        dma16(live ? va.rs : rs_none, st + j * 1024, offa[j], ka_next * sa);
+      else
+        dma16(live ? vb.rs : rs_none, st + OPB + (j - DMA_PER_OP) * 1024, offb[j - DMA_PER_OP],
+              (kb + kt) * sb);
+      if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
     };
     auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
 
@@ -448,31 +568,60 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     wait_vm<0>();
     __syncthreads();
     if (KT > 0) {
-      for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
-      if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
-      else if (KT == 2) wait_vm<DMA_PER_STEP>();
-      else wait_vm<0>();
+      if constexpr (Cfg<T>::KS == 2) {
+        // always three steps in flight (empty copies past the end), so the
+        // wait counts below hold for every K step
+#pragma unroll
+        for (int kt = 0; kt < STAGES - 1; ++kt)
+#pragma unroll
+          for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
+        wait_vm<2 * DMA_PER_STEP>();
+      } else {
+        for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+        if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
+        else if (KT == 2) wait_vm<DMA_PER_STEP>();
+        else wait_vm<0>();
+      }
       __syncthreads();
       if constexpr (Cfg<T>::KS == 2) {
-        // two fragment sets in ping-pong: the k-step 1 fragments load while
-        // k-step 0 multiplies, and the next stage's k-step 0 fragments load
-        // (after the barrier) while k-step 1 multiplies
+        // two fragment sets in ping-pong.  Each half K step's 16 MFMAs carry
+        // the other work woven between them (pinned by scheduling barriers),
+        // so the matrix pipe never waits on a burst of LDS reads or copy
+        // issues: the first half loads the second half's fragments, the
+        // second half (after the barrier) issues the copies of step kt+3 and
+        // loads the first half fragments of step kt+1.  Steps past the end
+        // copy through the empty descriptor, so every step looks the same.
         Frags<T, A_MN, B_MN> f0, f1;
         f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
         for (int kt = 0; kt < KT; ++kt) {
-          f1.load(stage(kt), stage(kt) + OPB, wm, wn, 1);
-          f0.mma(acc);
-          if (kt + 1 < KT) {
-            // K step kt+1 has landed once at most one later step of this
-            // wave's copies is outstanding; the barrier extends that to all
-            // waves and retires every read of the stage refilled next
-            if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
-            else wait_vm<0>();
-            __syncthreads();
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-            f0.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
-          }
-          f1.mma(acc);
+          const char* cs = stage(kt);
+          const char* ns = stage(kt + 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          // K step kt+1 has landed once at most one later step of this wave's
+          // copies is outstanding; the barrier extends that to all waves and
+          // retires every read of the stage refilled next
+          wait_vm<DMA_PER_STEP>();
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < DMA_PER_STEP) issue1(kt + STAGES - 1, q);
+              else if (q - DMA_PER_STEP < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q - DMA_PER_STEP);
+              __builtin_amdgcn_sched_barrier(0);
+            }
         }
       } else {
         Frags<T, A_MN, B_MN> cur, nxt;
@@ -499,7 +648,9 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     }
 
     // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
-    // every HBM access is a 16-byte row chunk
+    // every HBM access is a 16-byte row chunk.  Slice s holds fragments 2s and
+    // 2s+1 of every wave (FWD1: s = 0 gate, s = 1 up columns).
+    wait_vm<0>();      // the empty copies past the last step have landed
     __syncthreads();   // every wave is done with the ring
     float* ep = (float*)smem;
     auto put = [&](auto fn0c, auto&& value) {
@@ -542,6 +693,101 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       }
       __syncthreads();
     };
+    auto acc_of = [&](int f, int fn, int r) { return acc[f][fn][r]; };
+
+    // ---- a cut tile: every workgroup on it parks its fp32 partial tile
+    // (row-major, [slice][256][128]) in its workspace slot; the last one to
+    // arrive sums all partials in workgroup order (deterministic) while it
+    // writes the output.  The accumulators are not touched on this path.
+    constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
+    int w_first = 0, w_last = -1;
+    if (!whole) {
+      w_first = wg_of(t_start);
+      w_last = wg_of(t_start + KTe - 1);
+      const int which = (r_beg >= t_start) ? 0 : 1;   // first or last tile of the range
+      const __amdgpu_buffer_rsrc_t pw =
+          make_rsrc((const char*)a.part + (long long)(2 * L + which) * SLOT, SLOT);
+      auto park = [&](int sl) {
+        return [&, sl](int row, int c, const float* v) {
+          const uint32_t off = (uint32_t)(((sl * BM + row) * 128 + c) * 4);
+          const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
+          // system-coherent (sc0 sc1) stores: visible to the other XCDs'
+          // L2s without writing back or invalidating whole caches
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), pw, off, 0,
+                                                 CPOL_SYS);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), pw, off + 16u, 0,
+                                                 CPOL_SYS);
+        };
+      };
+      put(std::integral_constant<int, 0>{}, acc_of);
+      take(park(0));
+      put(std::integral_constant<int, 2>{}, acc_of);
+      take(park(1));
+      wait_vm<0>();   // this wave's partial stores have completed
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(a.cnt + w_first, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == w_last - w_first;
+        if (last) __hip_atomic_store(a.cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      if (!s_last) continue;
+    }
+    // sum of the parked partials of slices sa (and sb >= 0) at (row, c):
+    // 4 row chunks per pass, one pass of loads per contributing workgroup
+    auto take_sum = [&](int sa, int sb, auto&& consume) {
+      for (int grp = 0; grp < 4; ++grp) {
+        float va[4][8], vb[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) va[u][e] = vb[u][e] = 0.f;
+        for (int w = w_first; w <= w_last; ++w) {
+          const int wh = (k0 + W * w / nsh >= t_start) ? 0 : 1;
+          const __amdgpu_buffer_rsrc_t pr =
+              make_rsrc((const char*)a.part + (long long)(2 * w + wh) * SLOT, SLOT);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int idx = (grp * 4 + u) * NT + tid;
+            const int row = idx >> 4, cc = (idx & 15) * 8;
+            const uint32_t oa = (uint32_t)(((sa * BM + row) * 128 + cc) * 4);
+            const f32x4 l0 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, oa, 0, CPOL_SYS));
+            const f32x4 h0 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, oa + 16u, 0, CPOL_SYS));
+            va[u][0] += l0.x; va[u][1] += l0.y; va[u][2] += l0.z; va[u][3] += l0.w;
+            va[u][4] += h0.x; va[u][5] += h0.y; va[u][6] += h0.z; va[u][7] += h0.w;
+            if (sb >= 0) {
+              const uint32_t ob = (uint32_t)(((sb * BM + row) * 128 + cc) * 4);
+              const f32x4 l1 = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, ob, 0, CPOL_SYS));
+              const f32x4 h1 = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, ob + 16u, 0, CPOL_SYS));
+              vb[u][0] += l1.x; vb[u][1] += l1.y; vb[u][2] += l1.z; vb[u][3] += l1.w;
+              vb[u][4] += h1.x; vb[u][5] += h1.y; vb[u][6] += h1.z; vb[u][7] += h1.w;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = (grp * 4 + u) * NT + tid;
+          consume(idx >> 4, (idx & 15) * 8, va[u], vb[u]);
+        }
+      }
+    };
+    // slice sl of the finished tile -> consume(row, c, v[8])
+    auto emit = [&](auto slc, auto&& consume) {
+      constexpr int sl = decltype(slc)::value;
+      if (whole) {
+        put(std::integral_constant<int, 2 * sl>{}, acc_of);
+        take(consume);
+      } else {
+        take_sum(sl, -1, [&](int row, int c, const float* v, const float*) { consume(row, c, v); });
+      }
+    };
+
     auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, const float* v) {
       if constexpr (sizeof(T) == 2) {
         buf_store16(rs, elem * 2u, pack16(v, T()));
@@ -567,34 +813,58 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
                                                   clamp_bytes((long long)rows * a.ldc * ES));
       const __amdgpu_buffer_rsrc_t ar = make_rsrc((char*)ab + (long long)rows0 * a.ldc2 * ES,
                                                   clamp_bytes((long long)rows * a.ldc2 * ES));
-      using Z = std::integral_constant<int, 0>;
-      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
-      take([&](int row, int c, const float* v) {
+      auto store_gate = [&](int row, int c, const float* v) {
         if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + n0 + c), v);
-      });
-      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn + 2][r]; });
-      take([&](int row, int c, const float* v) {
+      };
+      auto store_up = [&](int row, int c, const float* v) {
         if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
-      });
-      // act = silu(g) * u in place of the gate accumulators
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int fn = 0; fn < FN / 2; ++fn)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float gv = acc[f][fn][r];
-            acc[f][fn][r] = gv * sigmoidf_(gv) * acc[f][fn + 2][r];
-          }
-      put(Z{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
-      take([&](int row, int c, const float* v) {
+      };
+      auto store_act = [&](int row, int c, const float* v) {
         if (row < rows && n0 + c < a.I) store8(ar, (uint32_t)(row * a.ldc2 + n0 + c), v);
-      });
+      };
+      if (whole) {
+        // gate slice out; then act = silu(g) * u replaces it in LDS (each
+        // lane rewrites the very words it put, so no barrier in between and
+        // the gate accumulators are dead once the slice is staged); up last
+        put(std::integral_constant<int, 0>{}, acc_of);
+        take(store_gate);
+        {
+          const int m = lane & 31;
+#pragma unroll
+          for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int rq = 0; rq < 4; ++rq) {
+                const int row = wm * WTM + f * 32 + m;
+                const int g = (wn * 64 + j * 32 + rq * 8 + (lane >> 5) * 4) >> 2;
+                f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
+                f32x4 v = *pp;
+                v.x = v.x * sigmoidf_(v.x) * acc[f][2 + j][rq * 4 + 0];
+                v.y = v.y * sigmoidf_(v.y) * acc[f][2 + j][rq * 4 + 1];
+                v.z = v.z * sigmoidf_(v.z) * acc[f][2 + j][rq * 4 + 2];
+                v.w = v.w * sigmoidf_(v.w) * acc[f][2 + j][rq * 4 + 3];
+                *pp = v;
+              }
+          __syncthreads();
+        }
+        take(store_act);
+        put(std::integral_constant<int, 2>{}, acc_of);
+        take(store_up);
+      } else {
+        take_sum(0, -1, [&](int row, int c, const float* v, const float*) { store_gate(row, c, v); });
+        take_sum(1, -1, [&](int row, int c, const float* v, const float*) { store_up(row, c, v); });
+        take_sum(0, 1, [&](int row, int c, const float* gv, const float* uv) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
+          store_act(row, c, v);
+        });
+      }
     } else {
       // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
       auto slice = [&](auto hc) {
         constexpr int h = decltype(hc)::value;
-        put(std::integral_constant<int, 2 * h>{}, [&](int f, int fn, int r) { return acc[f][fn][r]; });
         if constexpr (MODE == DX1) {
           const void* hb = sh ? a.sAux : a.aux;
           void* db = sh ? a.sC : a.C;
@@ -602,7 +872,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
           const __amdgpu_buffer_rsrc_t dr = make_rsrc(
               (char*)db + (long long)rows0 * a.ldc * ES, clamp_bytes((long long)rows * a.ldc * ES));
-          take([&](int row, int c, const float* d) {
+          emit(hc, [&](int row, int c, const float* d) {
             const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
             if (row < rows && i < a.I) {
               float gv[8], uv[8], dg[8], du[8];
@@ -636,7 +906,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           }
           const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, clamp_bytes(cbytes));
           const bool f32out = a.out_f32;
-          take([&](int row, int c, const float* v) {
+          emit(hc, [&](int row, int c, const float* v) {
             const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
             const int m = m0 + row;
             if (m < lim_m && n < a.N) {
@@ -659,10 +929,23 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 
 // ---------------------------------------------------------------- host side
 
+__global__ void zero_counters_kernel(int* cnt, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = 0;
+}
+
+int grid_size() {
+  const int n = moe_cu_count();
+  return n >= 8 ? (n / 8) * 8 : n;
+}
+
 template <typename T, int MODE>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
-  int grid = moe_cu_count();
-  grid = grid >= 8 ? (grid / 8) * 8 : grid;
+  const int grid = grid_size();
+  if (a.cnt) {
+    // counters must start at zero (a fill kernel, safe inside graph capture)
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(256), 0, s, a.cnt, grid);
+    MOE_TRY(moe_check_launch(what));
+  }
   hipLaunchKernelGGL((gmm_kernel<T, MODE>), dim3(grid), dim3(NT), 0, s, a);
   return moe_check_launch(what);
 }
@@ -696,6 +979,22 @@ int gmm_checks(const char* fn, const int32_t* offsets, int g0, int G, int R, int
   return MOE_OK;
 }
 
+constexpr size_t WS_CNT_BYTES = 4096;   // counters (<= 1024 workgroups)
+
+size_t ws_bytes_needed() { return WS_CNT_BYTES + (size_t)2 * grid_size() * BM * BN * 4; }
+
+// Attach a split-tile workspace (NULL: whole tiles only).
+int attach_ws(GmmArgs& a, void* ws, size_t ws_bytes, const char* fn) {
+  if (ws == nullptr) return MOE_OK;
+  MOE_TRY(moe_need_ptr(ws, fn, "ws", 256));
+  if (ws_bytes < ws_bytes_needed())
+    return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
+                    ws_bytes_needed());
+  a.cnt = (int*)ws;
+  a.part = (float*)((char*)ws + WS_CNT_BYTES);
+  return MOE_OK;
+}
+
 GmmArgs base_args(const int32_t* offsets, int g0, int G, int R, const moe_shared_expert* sh) {
   GmmArgs a = {};
   a.offsets = offsets;
@@ -709,10 +1008,13 @@ GmmArgs base_args(const int32_t* offsets, int g0, int G, int R, const moe_shared
 
 }  // namespace
 
+extern "C" size_t moe_gmm_workspace_bytes(void) { return ws_bytes_needed(); }
+
 extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
                                     int dt, int H, int I, const void* w13, const void* w2,
                                     void* h13, void* act, void* yp,
-                                    const moe_shared_expert* sh, moe_stream_t stream) {
+                                    const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                    moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_fwd";
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0 && R > 0) {
@@ -735,6 +1037,7 @@ extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int 
   if (!use_sh && (G == 0 || R == 0)) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   GmmArgs a = base_args(offsets, g0, (R > 0) ? G : 0, R, sh);
+  MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
   // FWD1: h13 = X . W13^T (N = 2I as I gate/up pairs, K = H)
   a.N = 2 * I; a.K = H; a.I = I;
   a.X = xp; a.ldx = H;
@@ -756,7 +1059,8 @@ extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int 
 extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G,
                                        int R, int dt, int H, int I, const void* w13,
                                        const void* w2, const void* h13, void* dh13, void* dxp,
-                                       const moe_shared_expert* sh, moe_stream_t stream) {
+                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                       moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_bwd_dx";
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0 && R > 0) {
@@ -779,6 +1083,7 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
   if (!use_sh && (G == 0 || R == 0)) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   GmmArgs a = base_args(offsets, g0, (R > 0) ? G : 0, R, sh);
+  MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
   // DX1: dact = dyp . W2 (W2 stored [K=H][N=I]), SwiGLU backward into dh13
   a.N = I; a.K = H; a.I = I;
   a.X = dyp; a.ldx = H;
@@ -800,7 +1105,8 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
 extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp,
                                        const void* dh13, const int32_t* offsets, int g0, int G,
                                        int R, int dt, int H, int I, void* dw13, void* dw2,
-                                       const moe_shared_expert* sh, moe_stream_t stream) {
+                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                       moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_bwd_dw";
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0) {
@@ -827,6 +1133,7 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
   if (!use_sh && G == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   GmmArgs a = base_args(offsets, g0, G, R, sh);
+  MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
   a.shared = use_sh ? 1 : 0;   // an empty shared expert still gets zero gradients
   a.shT = use_sh ? sh->T : 0;
   // dW2[e] [H,I] = dyp_e^T . act_e
@@ -845,6 +1152,8 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
   return launch_dt<DW>(dt, a, s, fn);
 }
 
+size_t moe_gmm_split_ws_bytes() { return ws_bytes_needed(); }
+
 // ---------------------------------------------------------------- router products
 // The fp32 router projection on the bf16 MFMA path (used for bf16 tokens):
 // the fp32 factor is split into three bf16 parts (hi + mid + lo carry all 24
@@ -853,8 +1162,9 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
 // added in fp64 by the caller, which keeps the result within a few fp32 ulps.
 
 int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, int H, int E, int S,
-                       hipStream_t s) {
+                       void* split_ws, hipStream_t s) {
   GmmArgs a = {};
+  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits");
   a.dense = 1; a.G = S; a.shT = T; a.R = T;
   a.N = E; a.K = 3 * (H / S); a.kwrap = H / S;
   a.X = x; a.ldx = H; a.x_gs = H / S;
@@ -864,8 +1174,9 @@ int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, 
 }
 
 int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, int E,
-                      hipStream_t s) {
+                      void* split_ws, hipStream_t s) {
   GmmArgs a = {};
+  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits_bwd");
   a.dense = 1; a.G = 1; a.shT = T; a.R = T;
   a.N = H; a.K = E;
   a.X = dlb; a.ldx = E;
@@ -875,8 +1186,9 @@ int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, 
 }
 
 int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, int H, int E, int S,
-                       hipStream_t s) {
+                       void* split_ws, hipStream_t s) {
   GmmArgs a = {};
+  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits_bwd");
   a.dense = 1; a.G = S; a.shT = 3 * (T / S); a.R = T;
   a.M = H; a.N = E; a.kwrap = T / S;
   a.X = x; a.ldx = H; a.x_gs = (long long)(T / S) * H;

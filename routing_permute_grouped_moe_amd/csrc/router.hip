@@ -228,12 +228,13 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // workspace layout (bytes), forward and backward use it separately
 struct RouterWs {
-  size_t wg3s, wgb, part, dl3s, dlb, colpart, total;
+  size_t split, wg3s, wgb, part, dl3s, dlb, colpart, total;
 };
 static RouterWs router_ws_layout(int T, int H, int E) {
   RouterWs w = {};
   const size_t he = (size_t)H * E, te = (size_t)T * E;
   size_t o = 0;
+  w.split = o; o += align256(moe_gmm_split_ws_bytes());
   w.wg3s = o; o += align256(3 * he * 2);
   w.wgb = o; o += align256(he * 2);
   w.part = o;
@@ -285,7 +286,7 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
     hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
                        wg3s, (bf16_t*)nullptr);
     MOE_TRY(moe_check_launch(fn));
-    MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, s));
+    MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, w + L.split, s));
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s,
                        (const float*)part, (long long)T * E, E, bias, logits);
     return moe_check_launch(fn);
@@ -344,8 +345,8 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
     hipLaunchKernelGGL(split_dl_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s, dlogits,
                        T, E, dl3s, dlb);
     MOE_TRY(moe_check_launch(fn));
-    MOE_TRY(moe_gmm_router_dx(dlb, wgb, dx, T, H, E, s));
-    MOE_TRY(moe_gmm_router_dwg(x, dl3s, part, T, H, E, RT_SPLIT, s));
+    MOE_TRY(moe_gmm_router_dx(dlb, wgb, dx, T, H, E, w + L.split, s));
+    MOE_TRY(moe_gmm_router_dwg(x, dl3s, part, T, H, E, RT_SPLIT, w + L.split, s));
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s,
                        (const float*)part, (long long)H * E, E, (const float*)nullptr, dwg);
     MOE_TRY(moe_check_launch(fn));

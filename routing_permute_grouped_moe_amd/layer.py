@@ -80,6 +80,10 @@ class MoeLayer:
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         self.rws_bytes = abi.moe_router_workspace_bytes(T, H, E, self.dt) if s.router else 0
         self.rws = torch.empty(max(self.rws_bytes, 256), dtype=torch.uint8, device=dev)
+        # K-split workspace of the grouped GEMM: off by default (whole tiles
+        # measure faster on the shapes here); enable_gemm_split() turns it on
+        self.gws_bytes = 0
+        self.gws = None
         self.h13 = e(R, 2 * I)
         self.act = e(R, I)
         self.yp = z(R, H)            # remote rows stay zero
@@ -108,6 +112,14 @@ class MoeLayer:
             self.dws2 = e(H, I)
 
     # ------------------------------------------------------------------ helpers
+    def enable_gemm_split(self, on: bool = True):
+        """Let the grouped GEMM cut the tiles of its last rounds along K."""
+        if on:
+            self.gws_bytes = abi.moe_gmm_workspace_bytes()
+            self.gws = torch.empty(self.gws_bytes, dtype=torch.uint8, device=self.device)
+        else:
+            self.gws_bytes, self.gws = 0, None
+
     def shared_desc(self):
         if not self.s.shared:
             return None
@@ -136,7 +148,8 @@ class MoeLayer:
         s = self.s
         sh = self.shared_desc() if shared is None else shared
         abi.moe_grouped_gemm_fwd(self.xp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H, s.I,
-                                 self.w13, self.w2, self.h13, self.act, self.yp, sh, stream)
+                                 self.w13, self.w2, self.h13, self.act, self.yp, sh, self.gws,
+                                 self.gws_bytes, stream)
 
     def combine(self, stream=None):
         s = self.s
@@ -154,14 +167,14 @@ class MoeLayer:
         sh = self.shared_desc() if shared is None else shared
         abi.moe_grouped_gemm_bwd_dx(self.dyp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H,
                                     s.I, self.w13, self.w2, self.h13, self.dh13, self.dxp, sh,
-                                    stream)
+                                    self.gws, self.gws_bytes, stream)
 
     def gmm_bwd_dw(self, stream=None, shared=None):
         s = self.s
         sh = self.shared_desc() if shared is None else shared
         abi.moe_grouped_gemm_bwd_dw(self.xp, self.act, self.dyp, self.dh13, self.offsets, s.g0,
                                     s.groups, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh,
-                                    stream)
+                                    self.gws, self.gws_bytes, stream)
 
     def route_bwd(self, stream=None):
         s = self.s

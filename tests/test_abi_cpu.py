@@ -102,10 +102,14 @@ def test_shape_limits(abi):
     assert st == abi.MOE_ERR_INVALID_ARG
     # grouped GEMM: I not a multiple of 64, window beyond 1024 experts
     st = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 0, 8, 64, 1, 128, 96, FAKE, FAKE, FAKE,
-                FAKE, FAKE, None, None)
+                FAKE, FAKE, None, None, 0, None)
     assert st == abi.MOE_ERR_UNSUPPORTED
     st = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 1000, 100, 64, 1, 128, 64, FAKE, FAKE,
-                FAKE, FAKE, FAKE, None, None)
+                FAKE, FAKE, FAKE, None, None, 0, None)
+    # a workspace that is too small
+    st2 = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 0, 8, 64, 1, 128, 64, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, None, FAKE, 4096, None)
+    assert st2 == abi.MOE_ERR_WORKSPACE
     assert st == abi.MOE_ERR_UNSUPPORTED
     # a row longer than the row kernels keep in registers
     st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 0, 4, 16384, 2, FAKE, None)

@@ -27,12 +27,13 @@ def near_tie_tokens(logits, k):
     return (s[:, k - 1] - s[:, k]) < 1e-5
 
 
-def check_layer(name, **overrides):
+def check_layer(name, split=False, **overrides):
     cfg = synth.get_config(name, **overrides)
-    print(f"\n[layer] config={cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}",
-          flush=True)
+    print(f"\n[layer] config={cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
+          f"gemm_split={split}", flush=True)
     inp = synth.make_inputs(cfg)
     L = make_layer(cfg, inp)
+    L.enable_gemm_split(split)
     L.forward()
     L.backward()
     torch.cuda.synchronize()
@@ -100,6 +101,12 @@ def test_layer_pangu_share_full_size():
     check_layer("pangu")
 
 
+def test_layer_pangu_share_full_size_gemm_split():
+    # the grouped GEMM with K-cut tail tiles (fp32 partial tiles summed in a
+    # fixed order by the last workgroup to arrive)
+    check_layer("pangu", split=True)
+
+
 def test_layer_deepseek_shape_reduced_width():
     # full token count, expert count, top-8 and Zipf(1.2) skew (empty and hot
     # experts); hidden sizes reduced so the oracle stays quick
@@ -111,10 +118,12 @@ def test_layer_stress_shape_reduced_width():
     check_layer("stress", H=512)
 
 
-def test_layer_step_is_bitwise_deterministic():
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+def test_layer_step_is_bitwise_deterministic(split):
     cfg = synth.get_config("small", T=1024)
     inp = synth.make_inputs(cfg)
     L = make_layer(cfg, inp)
+    L.enable_gemm_split(split)
     outs = []
     for _ in range(2):
         L.step()

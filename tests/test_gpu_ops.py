@@ -218,11 +218,16 @@ GMM_CASES = [
     ([0, 0, 0], 128, 64, 0, None, 0, "bf16"),
     ([1000], 384, 320, 0, None, 0, "bf16"),
     ([], 256, 128, 0, 0, 300, "bf16"),
+    # 150 small groups: more than two rounds of tiles on a 256-CU grid, so
+    # whole round-robin tiles and K-cut tail tiles meet in one launch
+    ([int(c) for c in np.random.default_rng(7).integers(0, 60, 150)], 1024, 512, 0, None, 40,
+     "bf16"),
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
 @pytest.mark.parametrize("counts,H,I,g0,G,shT,dt", GMM_CASES)
-def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt):
+def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt, split):
     r = _rng(sum(counts) + H + I + g0)
     E = len(counts)
     G = E - g0 if G is None else G
@@ -254,17 +259,20 @@ def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt):
                    y=z(shT, H), dy=SDY, dh13=z(shT, 2 * I), dx=z(shT, H), dw13=z(2 * I, H),
                    dw2=z(H, I))
         sh = abi.shared_expert(T=shT, **shb)
-    abi.moe_grouped_gemm_fwd(XP, OFF, g0, G, R, code, H, I, W13, W2, h13, act, yp, sh)
+    wsb = abi.moe_gmm_workspace_bytes() if split else 0
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda") if split else None
+    abi.moe_grouped_gemm_fwd(XP, OFF, g0, G, R, code, H, I, W13, W2, h13, act, yp, sh, ws, wsb)
     torch.cuda.synchronize()
-    ws = lambda g: w13[g]
     rh13, ract, ryp = oracle.grouped_forward(xp, offsets, w13, w2, g0, G) if E else \
         (np.zeros((R, 2 * I)), np.zeros((R, I)), np.zeros((R, H)))
     assert rel_err(host(h13), rh13) <= tol
     assert rel_err(host(act), ract) <= tol
     assert rel_err(host(yp), ryp) <= tol
     # backward dX / dW on the GPU's own saved activations
-    abi.moe_grouped_gemm_bwd_dx(DYP, OFF, g0, G, R, code, H, I, W13, W2, h13, dh13, dxp, sh)
-    abi.moe_grouped_gemm_bwd_dw(XP, act, DYP, dh13, OFF, g0, G, R, code, H, I, dw13, dw2, sh)
+    abi.moe_grouped_gemm_bwd_dx(DYP, OFF, g0, G, R, code, H, I, W13, W2, h13, dh13, dxp, sh, ws,
+                                wsb)
+    abi.moe_grouped_gemm_bwd_dw(XP, act, DYP, dh13, OFF, g0, G, R, code, H, I, dw13, dw2, sh, ws,
+                                wsb)
     torch.cuda.synchronize()
     if E:
         rdh13, rdxp, rdw13, rdw2 = oracle.grouped_backward(xp, dyp, offsets, w13, w2, g0, G)
