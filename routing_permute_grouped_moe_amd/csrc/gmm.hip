@@ -44,10 +44,7 @@ namespace {
 constexpr int BM = 256, BN = 256, NT = 256;
 constexpr int WTM = 128, WTN = 128;  // wave tile
 constexpr int FM = 4, FN = 4;        // 32x32 fragments per wave tile
-constexpr int STAGES = 4;            // LDS ring depth (3 K steps in flight)
-constexpr int OPB = 16384;           // bytes of one operand tile in one stage
-constexpr int STAGE_BYTES = 2 * OPB;
-constexpr int DMA_PER_OP = OPB / 1024 / (NT / 64);   // 1 KB copies per wave per operand
+constexpr int RING_BYTES = 131072;   // LDS ring of operand stages (also the epilogue slice)
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
 constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
 constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer range
@@ -78,23 +75,32 @@ struct GmmArgs {
   float* part;   // 2 partial tiles (256 x 256 fp32) per workgroup
 };
 
+// Per element type: K step BK (KS MFMA k-steps), ring of STAGES stages of two
+// OPB-byte operand tiles, ROWB bytes per K-major tile row, DPO 1 KB copies
+// per wave per operand per K step.
 template <typename T> struct Cfg;
 template <> struct Cfg<bf16_t> {
   static constexpr int ES = 2, VEC = 8, BK = 32, KS = 2;   // 2 MFMA k-steps of 16
+  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64, DPO = OPB / 1024 / (NT / 64);
 };
 template <> struct Cfg<float> {
   static constexpr int ES = 4, VEC = 4, BK = 16, KS = 8;   // 8 MFMA k-steps of 2
+  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64, DPO = OPB / 1024 / (NT / 64);
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_t;
 
-// K-major stage tile: 256 rows x 64 bytes; 16-byte chunk c of row r lives in
-// slot c ^ ((r >> 2) & 3), so 16 consecutive rows read at one chunk hit 16
-// distinct 16-byte bank groups.
-__device__ __forceinline__ int kslot_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+// K-major stage tile: 256 rows x ROWB bytes; 16-byte chunk c of row r lives
+// in slot c ^ kswz(r), so the 16 rows that one pass of a 16-byte LDS read
+// serves (16 lanes, 256 bytes of banks) hit 16 distinct bank groups.
+template <typename T> __device__ __forceinline__ int kswz(int row) {
+  static_assert(Cfg<T>::ROWB == 64, "64-byte rows: 4 rows per 256 bytes of banks");
+  return (row >> 2) & 3;
+}
+template <typename T> __device__ __forceinline__ int kslot_off(int row, int chunk) {
+  return row * Cfg<T>::ROWB + ((chunk ^ kswz<T>(row)) << 4);
 }
 // MN-major stage tile (bf16): 32 K rows x 512 bytes; 16-byte chunk c of row k
 // lives in slot c ^ (4 * (k & 3)), so the four rows of one transpose read
@@ -124,7 +130,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 __device__ __forceinline__ void dma16(const i32x4& rs, uint32_t lds, uint32_t voff, int soff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(uniform((int)lds))
+               : "v"(voff), "s"(rs), "s"(uniform(soff)), "{m0}"(uniform((int)lds))
                : "memory");
 }
 
@@ -160,21 +166,23 @@ __device__ __forceinline__ View make_view(const void* base, long long bytes, int
 }
 
 // ---------------------------------------------------------------- HBM -> LDS
-// One operand tile of one K step is 16 copies of 1 KB, DMA_PER_OP per wave.
-// The per-lane byte offsets of a tile are fixed; a K step only moves the
-// uniform offset (k0 * ES for K-major, k0 * ld * ES for MN-major).
+// One operand tile of one K step is OPB / 1 KB copies, DPO per wave.  The
+// per-lane byte offsets of a tile are fixed; a K step only moves the uniform
+// offset (k0 * ES for K-major, k0 * ld * ES for MN-major).
 //
-// K-major: copy q covers rows 16q..16q+15; lane l fills row 16q + l/4, slot l%4.
+// K-major: a copy covers 1024 / ROWB whole rows; lane l fills row
+// q * RPC + l / LPR, slot l % LPR, from the chunk that belongs in that slot.
 template <typename T, bool SWIGLU>
 __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
-                                               uint32_t (&off)[DMA_PER_OP]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
+                                               uint32_t (&off)[Cfg<T>::DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
+  constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;   // lanes per row, rows per copy
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OP; ++j) {
-    const int q = wave * DMA_PER_OP + j;
-    const int row = q * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+  for (int j = 0; j < DPO; ++j) {
+    const int q = wave * DPO + j;
+    const int row = q * RPC + lane / LPR;
+    const int chunk = (lane % LPR) ^ kswz<T>(row);
     int src;
     bool ok;
     if (SWIGLU) {
@@ -196,12 +204,12 @@ __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
 // l%32); fp32 copy q covers K row q (lane l: slot l).
 template <typename T>
 __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
-                                                uint32_t (&off)[DMA_PER_OP]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
+                                                uint32_t (&off)[Cfg<T>::DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OP; ++j) {
-    const int q = wave * DMA_PER_OP + j;
+  for (int j = 0; j < DPO; ++j) {
+    const int q = wave * DPO + j;
     int k, chunk;
     if constexpr (sizeof(T) == 2) {
       k = 2 * q + (lane >> 5);
@@ -215,12 +223,13 @@ __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
   }
 }
 
+template <int DPO>
 __device__ __forceinline__ void issue_op(const View& v, const char* lds_op,
-                                         const uint32_t (&off)[DMA_PER_OP], int soff) {
+                                         const uint32_t (&off)[DPO], int soff) {
   const int wave = threadIdx.x >> 6;
-  const uint32_t base = lds_addr(lds_op) + wave * DMA_PER_OP * 1024;
+  const uint32_t base = lds_addr(lds_op) + wave * DPO * 1024;
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OP; ++j) dma16(v.rs, base + j * 1024, off[j], soff);
+  for (int j = 0; j < DPO; ++j) dma16(v.rs, base + j * 1024, off[j], soff);
 }
 
 // ---------------------------------------------------------------- LDS -> MFMA
@@ -231,7 +240,7 @@ __device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
   const int lane = threadIdx.x & 63;
   if constexpr (sizeof(T) == 2) {
     if constexpr (!MN) {
-      return *(const u32x4*)(lds + kslot_off(r0 + (lane & 31), ks * 2 + (lane >> 5)));
+      return *(const u32x4*)(lds + kslot_off<T>(r0 + (lane & 31), ks * 2 + (lane >> 5)));
     } else {
       // transpose read: in a group of 16 lanes, lane i points at row k0 + i/4,
       // columns c0 + 4 (i%4) .. +3 and receives column c0 + i of rows k0..k0+3
@@ -250,7 +259,7 @@ __device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
     const int k = ks * 2 + (lane >> 5);
     const int r = r0 + (lane & 31);
     if constexpr (!MN) {
-      return *(const float*)(lds + kslot_off(r, k >> 2) + (k & 3) * 4);
+      return *(const float*)(lds + kslot_off<T>(r, k >> 2) + (k & 3) * 4);
     } else {
       return *(const float*)(lds + k * 1024 + r * 4);
     }
@@ -286,7 +295,10 @@ struct Frags {
   }
 };
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// logistic function: hardware exp2 and reciprocal (about 2 ulp), no IEEE divide
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ---------------------------------------------------------------- the kernel
 template <typename T, int MODE>
@@ -294,10 +306,13 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
+  constexpr int STAGES = Cfg<T>::STAGES, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
+  constexpr int DMA_PER_OP = Cfg<T>::DPO;
   constexpr int DMA_PER_STEP = 2 * DMA_PER_OP;   // buffer loads per wave per K step
+  static_assert(STAGES * STAGE_BYTES == RING_BYTES, "stage ring size");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-  static_assert(BM * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue slice must fit the ring");
+  __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
+  static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
   __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
   __shared__ int g_kp[MOE_MAX_E + 2];   // DW: K steps before each group in work order
   __shared__ int s_last;
@@ -415,13 +430,21 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       return g_kp[p] + (long long)(t % per) * max(1, (g_hi[gg] - g_lo[gg] + BK - 1) / BK);
     }
   };
-  const int rounds = total / nwg;
-  const int dp_tiles = (a.part != nullptr && total % nwg != 0) ? max(0, rounds - 1) * nwg : total;
+  // The K cut pays only when the last round of whole tiles would leave most
+  // workgroups idle (fewer than half of them busy); otherwise the partial
+  // tiles' extra traffic costs more than the idle time it removes.
+  const int rounds = total / nwg, rem = total % nwg;
+  const int dp_tiles =
+      (a.part != nullptr && rounds >= 1 && rem != 0 && 2 * rem < nwg) ? (rounds - 1) * nwg : total;
   const long long k0 = uniform(kstart(dp_tiles));
   const long long W = uniform(kstart(total)) - k0;   // K steps of the cut region
-  // every sharing workgroup gets at least one K step (no empty ranges, so
-  // every workgroup counted on a cut tile does arrive)
-  const int nsh = (int)min((long long)nwg, W);
+  // K steps of the region's longest tile (its first one: M-var tiles are all
+  // alike, dW tiles come in descending order of their K steps).  Ranges are
+  // at least that long, so a boundary falls inside a tile at most once:
+  // every cut tile has exactly two partial sums, and their fp32 sum does not
+  // depend on which of the two workgroups adds them (deterministic result).
+  const long long kmax = dp_tiles < total ? uniform(kstart(dp_tiles + 1)) - k0 : 1;
+  const int nsh = (int)min((long long)nwg, W / kmax);
   const bool active = L < nsh;
   const long long r_beg = active ? k0 + W * L / nsh : 0;
   const long long r_end = active ? k0 + W * (L + 1) / nsh : 0;
@@ -568,7 +591,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     wait_vm<0>();
     __syncthreads();
     if (KT > 0) {
-      if constexpr (Cfg<T>::KS == 2) {
+      if constexpr (sizeof(T) == 2) {
         // always three steps in flight (empty copies past the end), so the
         // wait counts below hold for every K step
 #pragma unroll
@@ -583,7 +606,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         else wait_vm<0>();
       }
       __syncthreads();
-      if constexpr (Cfg<T>::KS == 2) {
+      if constexpr (sizeof(T) == 2) {
         // two fragment sets in ping-pong.  Each half K step's 16 MFMAs carry
         // the other work woven between them (pinned by scheduling barriers),
         // so the matrix pipe never waits on a burst of LDS reads or copy
@@ -650,16 +673,74 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
     // every HBM access is a 16-byte row chunk.  Slice s holds fragments 2s and
     // 2s+1 of every wave (FWD1: s = 0 gate, s = 1 up columns).
+    // ---- a cut tile: both workgroups on it park their fp32 partial tile in
+    // the accumulator layout (each lane's 64 16-byte chunks, coalesced); the
+    // second to arrive goes on to the epilogue, which adds the other's partial
+    // chunk by chunk as it stages the accumulators, and the first moves on to
+    // its next tile.
+    constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
+    auto chunk_off = [&](int i, int j, int q) {
+      return (uint32_t)((((i * FN + j) * 4 + q) * NT + (int)threadIdx.x) * 16);
+    };
+    __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, 0);   // partner's partial tile
+    const bool fix = !whole;
+    if (!whole) {
+      const int w_first = wg_of(t_start);   // range holding the tile's first step
+      const int which = (r_beg >= t_start) ? 0 : 1;   // first or last tile of the range
+      const __amdgpu_buffer_rsrc_t pw =
+          make_rsrc((const char*)a.part + (long long)(2 * L + which) * SLOT, SLOT);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                             acc[i][j][4 * q + 3]};
+            // system-coherent (sc0 sc1) stores: visible to the other XCDs'
+            // L2s without writing back or invalidating whole caches
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pw,
+                                                   chunk_off(i, j, q), 0, CPOL_SYS);
+          }
+        __builtin_amdgcn_sched_barrier(0);   // a few accumulators out at a time
+      }
+      wait_vm<0>();   // this wave's partial stores have completed
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(a.cnt + w_first, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == 1;
+        if (last) __hip_atomic_store(a.cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      if (!s_last) continue;
+      // the other workgroup and the slot it parked this tile in
+      const int partner = (L == w_first) ? w_first + 1 : w_first;
+      const int ph = (k0 + W * partner / nsh >= t_start) ? 0 : 1;
+      pr = make_rsrc((const char*)a.part + (long long)(2 * partner + ph) * SLOT, SLOT);
+    }
+
+    // a per-tile copy of the thread index: the epilogue's address arithmetic
+    // then belongs to this tile and is not kept live (and spilled) across
+    // the persistent loop as an invariant
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int elane = etid & 63;
     wait_vm<0>();      // the empty copies past the last step have landed
     __syncthreads();   // every wave is done with the ring
     float* ep = (float*)smem;
+    auto partner_chunk = [&](int f, int fn, int rq) {
+      return __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, chunk_off(f, fn, rq), 0, CPOL_SYS));
+    };
     auto put = [&](auto fn0c, auto&& value) {
       // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
       // (fn0 is a compile-time constant so the accumulators stay in registers);
       // 16-byte granule g of row m sits at g ^ (m % 32), so the 32 rows of a
       // store and the 16 chunks of a row read all hit distinct banks
       constexpr int slice_fn0 = decltype(fn0c)::value;
-      const int m = lane & 31;
+      const int m = elane & 31;
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -667,7 +748,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             const int row = wm * WTM + f * 32 + m;
-            const int g = (wn * 64 + j * 32 + rq * 8 + (lane >> 5) * 4) >> 2;
+            const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
             f32x4 v;
             v.x = value(f, slice_fn0 + j, rq * 4 + 0);
             v.y = value(f, slice_fn0 + j, rq * 4 + 1);
@@ -677,11 +758,35 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           }
       __syncthreads();
     };
+    // a cut tile: add the other workgroup's partial of fragments fn0, fn0+1
+    // to the staged slice (each lane updates the words it put)
+    auto add_partner = [&](auto fn0c) {
+      if (!fix) return;
+      constexpr int slice_fn0 = decltype(fn0c)::value;
+      const int m = elane & 31;
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        f32x4 pv[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) pv[j][rq] = partner_chunk(f, slice_fn0 + j, rq);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int row = wm * WTM + f * 32 + m;
+            const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
+            *(f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2)) += pv[j][rq];
+          }
+      }
+      __syncthreads();
+    };
     auto take = [&](auto&& consume) {
       // 256 rows x 16 chunks of 8 columns, 16 per thread
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
-        const int idx = it * NT + tid;
+        const int idx = it * NT + etid;
         const int row = idx >> 4, cc = (idx & 15) * 8;
         const int sw = row & 31;
         float v[8];
@@ -695,97 +800,12 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     };
     auto acc_of = [&](int f, int fn, int r) { return acc[f][fn][r]; };
 
-    // ---- a cut tile: every workgroup on it parks its fp32 partial tile
-    // (row-major, [slice][256][128]) in its workspace slot; the last one to
-    // arrive sums all partials in workgroup order (deterministic) while it
-    // writes the output.  The accumulators are not touched on this path.
-    constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
-    int w_first = 0, w_last = -1;
-    if (!whole) {
-      w_first = wg_of(t_start);
-      w_last = wg_of(t_start + KTe - 1);
-      const int which = (r_beg >= t_start) ? 0 : 1;   // first or last tile of the range
-      const __amdgpu_buffer_rsrc_t pw =
-          make_rsrc((const char*)a.part + (long long)(2 * L + which) * SLOT, SLOT);
-      auto park = [&](int sl) {
-        return [&, sl](int row, int c, const float* v) {
-          const uint32_t off = (uint32_t)(((sl * BM + row) * 128 + c) * 4);
-          const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
-          // system-coherent (sc0 sc1) stores: visible to the other XCDs'
-          // L2s without writing back or invalidating whole caches
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), pw, off, 0,
-                                                 CPOL_SYS);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), pw, off + 16u, 0,
-                                                 CPOL_SYS);
-        };
-      };
-      put(std::integral_constant<int, 0>{}, acc_of);
-      take(park(0));
-      put(std::integral_constant<int, 2>{}, acc_of);
-      take(park(1));
-      wait_vm<0>();   // this wave's partial stores have completed
-      __syncthreads();
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(a.cnt + w_first, 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old == w_last - w_first;
-        if (last) __hip_atomic_store(a.cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last ? 1 : 0;
-      }
-      __syncthreads();
-      if (!s_last) continue;
-    }
-    // sum of the parked partials of slices sa (and sb >= 0) at (row, c):
-    // 4 row chunks per pass, one pass of loads per contributing workgroup
-    auto take_sum = [&](int sa, int sb, auto&& consume) {
-      for (int grp = 0; grp < 4; ++grp) {
-        float va[4][8], vb[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) va[u][e] = vb[u][e] = 0.f;
-        for (int w = w_first; w <= w_last; ++w) {
-          const int wh = (k0 + W * w / nsh >= t_start) ? 0 : 1;
-          const __amdgpu_buffer_rsrc_t pr =
-              make_rsrc((const char*)a.part + (long long)(2 * w + wh) * SLOT, SLOT);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int idx = (grp * 4 + u) * NT + tid;
-            const int row = idx >> 4, cc = (idx & 15) * 8;
-            const uint32_t oa = (uint32_t)(((sa * BM + row) * 128 + cc) * 4);
-            const f32x4 l0 = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, oa, 0, CPOL_SYS));
-            const f32x4 h0 = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, oa + 16u, 0, CPOL_SYS));
-            va[u][0] += l0.x; va[u][1] += l0.y; va[u][2] += l0.z; va[u][3] += l0.w;
-            va[u][4] += h0.x; va[u][5] += h0.y; va[u][6] += h0.z; va[u][7] += h0.w;
-            if (sb >= 0) {
-              const uint32_t ob = (uint32_t)(((sb * BM + row) * 128 + cc) * 4);
-              const f32x4 l1 = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, ob, 0, CPOL_SYS));
-              const f32x4 h1 = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, ob + 16u, 0, CPOL_SYS));
-              vb[u][0] += l1.x; vb[u][1] += l1.y; vb[u][2] += l1.z; vb[u][3] += l1.w;
-              vb[u][4] += h1.x; vb[u][5] += h1.y; vb[u][6] += h1.z; vb[u][7] += h1.w;
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int idx = (grp * 4 + u) * NT + tid;
-          consume(idx >> 4, (idx & 15) * 8, va[u], vb[u]);
-        }
-      }
-    };
     // slice sl of the finished tile -> consume(row, c, v[8])
     auto emit = [&](auto slc, auto&& consume) {
       constexpr int sl = decltype(slc)::value;
-      if (whole) {
-        put(std::integral_constant<int, 2 * sl>{}, acc_of);
-        take(consume);
-      } else {
-        take_sum(sl, -1, [&](int row, int c, const float* v, const float*) { consume(row, c, v); });
-      }
+      put(std::integral_constant<int, 2 * sl>{}, acc_of);
+      add_partner(std::integral_constant<int, 2 * sl>{});
+      take(consume);
     };
 
     auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, const float* v) {
@@ -805,7 +825,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       }
     };
     if constexpr (MODE == FWD1) {
-      // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + lane%32,
+      // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + elane%32,
       // fragments 2,3 the matching up columns; LDS column c is i = i0 + c
       void* hb = sh ? a.sC : a.C;
       void* ab = sh ? a.sC2 : a.C2;
@@ -822,45 +842,39 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       auto store_act = [&](int row, int c, const float* v) {
         if (row < rows && n0 + c < a.I) store8(ar, (uint32_t)(row * a.ldc2 + n0 + c), v);
       };
-      if (whole) {
-        // gate slice out; then act = silu(g) * u replaces it in LDS (each
-        // lane rewrites the very words it put, so no barrier in between and
-        // the gate accumulators are dead once the slice is staged); up last
-        put(std::integral_constant<int, 0>{}, acc_of);
-        take(store_gate);
-        {
-          const int m = lane & 31;
+      // gate slice out; then act = silu(g) * u replaces it in LDS (each
+      // elane rewrites the very words it put, so no barrier in between and
+      // the gate accumulators are dead once the slice is staged); up last
+      put(std::integral_constant<int, 0>{}, acc_of);
+      add_partner(std::integral_constant<int, 0>{});
+      take(store_gate);
+      {
+        const int m = elane & 31;
 #pragma unroll
-          for (int f = 0; f < FM; ++f)
+        for (int f = 0; f < FM; ++f)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-              for (int rq = 0; rq < 4; ++rq) {
-                const int row = wm * WTM + f * 32 + m;
-                const int g = (wn * 64 + j * 32 + rq * 8 + (lane >> 5) * 4) >> 2;
-                f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
-                f32x4 v = *pp;
-                v.x = v.x * sigmoidf_(v.x) * acc[f][2 + j][rq * 4 + 0];
-                v.y = v.y * sigmoidf_(v.y) * acc[f][2 + j][rq * 4 + 1];
-                v.z = v.z * sigmoidf_(v.z) * acc[f][2 + j][rq * 4 + 2];
-                v.w = v.w * sigmoidf_(v.w) * acc[f][2 + j][rq * 4 + 3];
-                *pp = v;
-              }
-          __syncthreads();
-        }
-        take(store_act);
-        put(std::integral_constant<int, 2>{}, acc_of);
-        take(store_up);
-      } else {
-        take_sum(0, -1, [&](int row, int c, const float* v, const float*) { store_gate(row, c, v); });
-        take_sum(1, -1, [&](int row, int c, const float* v, const float*) { store_up(row, c, v); });
-        take_sum(0, 1, [&](int row, int c, const float* gv, const float* uv) {
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
-          store_act(row, c, v);
-        });
+            for (int rq = 0; rq < 4; ++rq) {
+              const int row = wm * WTM + f * 32 + m;
+              const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
+              f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
+              f32x4 v = *pp;
+              f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
+                         acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
+              if (fix) u += partner_chunk(f, 2 + j, rq);
+              v.x = v.x * sigmoidf_(v.x) * u.x;
+              v.y = v.y * sigmoidf_(v.y) * u.y;
+              v.z = v.z * sigmoidf_(v.z) * u.z;
+              v.w = v.w * sigmoidf_(v.w) * u.w;
+              *pp = v;
+            }
+        __syncthreads();
       }
+      take(store_act);
+      put(std::integral_constant<int, 2>{}, acc_of);
+      add_partner(std::integral_constant<int, 2>{});
+      take(store_up);
     } else {
       // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
       auto slice = [&](auto hc) {
@@ -872,22 +886,70 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
           const __amdgpu_buffer_rsrc_t dr = make_rsrc(
               (char*)db + (long long)rows0 * a.ldc * ES, clamp_bytes((long long)rows * a.ldc * ES));
-          emit(hc, [&](int row, int c, const float* d) {
-            const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
-            if (row < rows && i < a.I) {
-              float gv[8], uv[8], dg[8], du[8];
-              load8(hr, (uint32_t)(row * a.ldaux + i), gv);
-              load8(hr, (uint32_t)(row * a.ldaux + a.I + i), uv);
+          // d(act) -> d(gate), d(up) of act = silu(gate) * up
+          auto bwd8 = [&](int row, int i, const float* d, const float* gv, const float* uv) {
+            float dg[8], du[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float sg = sigmoidf_(gv[e]);
-                dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
-                du[e] = d[e] * gv[e] * sg;
-              }
-              store8(dr, (uint32_t)(row * a.ldc + i), dg);
-              store8(dr, (uint32_t)(row * a.ldc + a.I + i), du);
+            for (int e = 0; e < 8; ++e) {
+              const float sg = sigmoidf_(gv[e]);
+              dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+              du[e] = d[e] * gv[e] * sg;
             }
-          });
+            store8(dr, (uint32_t)(row * a.ldc + i), dg);
+            store8(dr, (uint32_t)(row * a.ldc + a.I + i), du);
+          };
+          if (sizeof(T) == 2) {
+            // bf16: the slice's gate/up chunks (16 per thread) are
+            // requested before the accumulators are staged, so their latency
+            // hides behind the LDS round trip instead of serializing with the
+            // stores (a load may not pass an earlier store to a buffer that
+            // could alias)
+            u32x4 graw[16], uraw[16];
+            auto fetch = [&](int it) {
+              const int idx = it * NT + etid;
+              const int row = idx >> 4, cc = (idx & 15) * 8;
+              const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+              const bool ok = row < rows && i < a.I;
+              graw[it] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + i) * 2u : OOB);
+              uraw[it] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + a.I + i) * 2u : OOB);
+            };
+            auto finish = [&](int it) {
+              const int idx = it * NT + etid;
+              const int row = idx >> 4, cc = (idx & 15) * 8;
+              const int sw = row & 31;
+              const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
+              const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
+              const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+              const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+              if (row < rows && i < a.I) {
+                float gv[8], uv[8];
+                unpack16(graw[it], gv, T());
+                unpack16(uraw[it], uv, T());
+                bwd8(row, i, d, gv, uv);
+              }
+            };
+            // first half requested before the staging, second half after it
+            // (ahead of the first half's stores)
+#pragma unroll
+            for (int it = 0; it < 8; ++it) fetch(it);
+            put(std::integral_constant<int, 2 * h>{}, acc_of);
+            add_partner(std::integral_constant<int, 2 * h>{});
+#pragma unroll
+            for (int it = 8; it < 16; ++it) fetch(it);
+#pragma unroll
+            for (int it = 0; it < 16; ++it) finish(it);
+            __syncthreads();
+          } else {
+            emit(hc, [&](int row, int c, const float* d) {
+              const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+              if (row < rows && i < a.I) {
+                float gv[8], uv[8];
+                load8(hr, (uint32_t)(row * a.ldaux + i), gv);
+                load8(hr, (uint32_t)(row * a.ldaux + a.I + i), uv);
+                bwd8(row, i, d, gv, uv);
+              }
+            });
+          }
         } else {
           // plain store: FWD2 / DX2 rows of C, or DW: dW[g] (M x N)
           void* cb;

@@ -134,6 +134,7 @@ static void launch_router_gemm(hipStream_t s, const TA* A, long long a_sm, long 
 #define RT_SPLIT 8   // K slices of the router products
 
 static bool mfma_path(int dt, int T, int H, int E) {
+  // each K slice a whole number of the grouped GEMM's 32-deep bf16 K steps
   return dt == MOE_BF16 && H % (RT_SPLIT * 32) == 0 && T % (RT_SPLIT * 32) == 0 && E % 64 == 0;
 }
 
