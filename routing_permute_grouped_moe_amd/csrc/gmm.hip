@@ -1214,7 +1214,6 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
   return launch_dt<DW>(dt, a, s, fn);
 }
 
-size_t moe_gmm_split_ws_bytes() { return ws_bytes_needed(); }
 
 // ---------------------------------------------------------------- router products
 // The fp32 router projection on the bf16 MFMA path (used for bf16 tokens):
@@ -1224,9 +1223,8 @@ size_t moe_gmm_split_ws_bytes() { return ws_bytes_needed(); }
 // added in fp64 by the caller, which keeps the result within a few fp32 ulps.
 
 int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, int H, int E, int S,
-                       void* split_ws, hipStream_t s) {
+                       hipStream_t s) {
   GmmArgs a = {};
-  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits");
   a.dense = 1; a.G = S; a.shT = T; a.R = T;
   a.N = E; a.K = 3 * (H / S); a.kwrap = H / S;
   a.X = x; a.ldx = H; a.x_gs = H / S;
@@ -1236,9 +1234,8 @@ int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, 
 }
 
 int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, int E,
-                      void* split_ws, hipStream_t s) {
+                      hipStream_t s) {
   GmmArgs a = {};
-  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits_bwd");
   a.dense = 1; a.G = 1; a.shT = T; a.R = T;
   a.N = H; a.K = E;
   a.X = dlb; a.ldx = E;
@@ -1248,9 +1245,8 @@ int moe_gmm_router_dx(const void* dlb, const void* wgb, void* dx, int T, int H, 
 }
 
 int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, int H, int E, int S,
-                       void* split_ws, hipStream_t s) {
+                       hipStream_t s) {
   GmmArgs a = {};
-  attach_ws(a, split_ws, ws_bytes_needed(), "moe_router_logits_bwd");
   a.dense = 1; a.G = S; a.shT = 3 * (T / S); a.R = T;
   a.M = H; a.N = E; a.kwrap = T / S;
   a.X = x; a.ldx = H; a.x_gs = (long long)(T / S) * H;

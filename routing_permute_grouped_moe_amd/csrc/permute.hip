@@ -149,7 +149,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
 #pragma unroll
     for (int i = 0; i < ROW_MAXC; ++i) {
       int q = q0 + i * ROW_THREADS + threadIdx.x;
-      v[i] = buf_load16(src, (uint32_t)q * 16u);
+      v[i] = buf_load16_nt(src, (uint32_t)q * 16u);
     }
     for (int j = 0; j < k; ++j) {
       const uint32_t rb = (uint32_t)rows[j] * row_bytes;
@@ -160,6 +160,22 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- gathers
+// The gathers below keep ROW_JB rows x ROW_QB chunks of loads in flight per
+// thread (requested together, then added in row order), so a token's k row
+// reads overlap instead of paying one HBM latency each.
+#define ROW_JB 8   // rows requested together
+#define ROW_QB 4   // 16-byte chunks per thread per pass
+
+// chunk q of row r (zero for q past the row); every row the gathers read is
+// read once, so the loads stream past the caches
+__device__ __forceinline__ u32x4 row_chunk(const __amdgpu_buffer_rsrc_t& rs, uint32_t rb, int q,
+                                           int nchunk) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (q < nchunk) v = buf_load16_nt(rs, rb + (uint32_t)q * 16u);
+  return v;
 }
 
 // ---------------------------------------------------------------- permute bwd
@@ -186,27 +202,53 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
                                         add0 ? row_bytes : 0);
   __amdgpu_buffer_rsrc_t a1 = make_rsrc(add1 ? (const char*)add1 + (long long)t * row_bytes : nullptr,
                                         add1 ? row_bytes : 0);
-  for (int q = threadIdx.x; q < nchunk; q += ROW_THREADS) {
-    float acc[VEC], tmp[VEC];
+  for (int q0 = threadIdx.x; q0 < nchunk; q0 += ROW_QB * ROW_THREADS) {
+    float acc[ROW_QB][VEC], tmp[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      u32x4 v = buf_load16(src, (uint32_t)rows[j] * row_bytes + (uint32_t)q * 16u);
-      unpack16(v, tmp, T());
+    for (int u = 0; u < ROW_QB; ++u)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += tmp[i];
+      for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += ROW_JB) {
+      u32x4 v[ROW_JB][ROW_QB];
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u) v[jj][u] = row_chunk(src, rb, q0 + u * ROW_THREADS, nchunk);
+        }
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u) {
+            unpack16(v[jj][u], tmp, T());
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[u][i] += tmp[i];
+          }
+        }
     }
-    if (add0) {
-      unpack16(buf_load16(a0, (uint32_t)q * 16u), tmp, T());
+    u32x4 e0[ROW_QB], e1[ROW_QB];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += tmp[i];
+    for (int u = 0; u < ROW_QB; ++u) {
+      e0[u] = add0 ? row_chunk(a0, 0, q0 + u * ROW_THREADS, nchunk) : u32x4{0u, 0u, 0u, 0u};
+      e1[u] = add1 ? row_chunk(a1, 0, q0 + u * ROW_THREADS, nchunk) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (add1) {
-      unpack16(buf_load16(a1, (uint32_t)q * 16u), tmp, T());
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += tmp[i];
+    for (int u = 0; u < ROW_QB; ++u) {
+      const int q = q0 + u * ROW_THREADS;
+      if (add0) {
+        unpack16(e0[u], tmp, T());
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[u][i] += tmp[i];
+      }
+      if (add1) {
+        unpack16(e1[u], tmp, T());
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[u][i] += tmp[i];
+      }
+      if (q < nchunk) buf_store16(out, (uint32_t)q * 16u, pack16(acc[u], T()));
     }
-    buf_store16(out, (uint32_t)q * 16u, pack16(acc, T()));
   }
 }
 
@@ -235,35 +277,59 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
   __amdgpu_buffer_rsrc_t out = make_rsrc((char*)y + (long long)t * row_bytes, row_bytes);
   __amdgpu_buffer_rsrc_t sh = make_rsrc(ys ? (const char*)ys + (long long)t * row_bytes : nullptr,
                                         ys ? row_bytes : 0);
-  for (int q = threadIdx.x; q < nchunk; q += ROW_THREADS) {
-    float acc[VEC], tmp[VEC];
-    if (ys) {
-      unpack16(buf_load16(sh, (uint32_t)q * 16u), acc, T());
-    } else {
+  for (int q0 = threadIdx.x; q0 < nchunk; q0 += ROW_QB * ROW_THREADS) {
+    float acc[ROW_QB][VEC], tmp[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    }
-    for (int j = 0; j < k; ++j) {
-      u32x4 v = buf_load16(src, (uint32_t)rows[j] * row_bytes + (uint32_t)q * 16u);
-      unpack16(v, tmp, T());
-      const float g = gates[j];
+    for (int u = 0; u < ROW_QB; ++u) {
+      if (ys) {
+        unpack16(row_chunk(sh, 0, q0 + u * ROW_THREADS, nchunk), acc[u], T());
+      } else {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += g * tmp[i];
+        for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
+      }
     }
-    buf_store16(out, (uint32_t)q * 16u, pack16(acc, T()));
+    for (int j0 = 0; j0 < k; j0 += ROW_JB) {
+      u32x4 v[ROW_JB][ROW_QB];
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u) v[jj][u] = row_chunk(src, rb, q0 + u * ROW_THREADS, nchunk);
+        }
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+          const float g = gates[j0 + jj];
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u) {
+            unpack16(v[jj][u], tmp, T());
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[u][i] += g * tmp[i];
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < ROW_QB; ++u) {
+      const int q = q0 + u * ROW_THREADS;
+      if (q < nchunk) buf_store16(out, (uint32_t)q * 16u, pack16(acc[u], T()));
+    }
   }
 }
 
 // dyp[row(t,j)] = gate[t,j] dy[t];  dgate[t,j] = <dy[t], yp[row(t,j)]>
+// (per thread fp32 partial dots over its chunks, then a fixed-order
+// reduction: wave sums, then the waves in order)
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ yp, const int32_t* __restrict__ row_id_map,
     const float* __restrict__ gate, int Tn, int H, int k, T* __restrict__ dyp,
     float* __restrict__ dgate) {
   constexpr int VEC = Elem<T>::VEC;
+  constexpr int NW = ROW_THREADS / MOE_WAVE;
   __shared__ int rows[MOE_MAX_E];
   __shared__ float gates[MOE_MAX_E];
-  __shared__ float red[ROW_THREADS / MOE_WAVE];
+  __shared__ float red[ROW_JB][NW];
   const int t = blockIdx.x;
   const long long R = (long long)Tn * k;
   for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
@@ -277,38 +343,59 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
   __amdgpu_buffer_rsrc_t din = make_rsrc((const char*)dy + (long long)t * row_bytes, row_bytes);
   __amdgpu_buffer_rsrc_t ypr = make_rsrc(yp, clamp_bytes(R * row_bytes));
   __amdgpu_buffer_rsrc_t dst = make_rsrc(dyp, clamp_bytes(R * row_bytes));
-  float d[ROW_MAXC][VEC];
-#pragma unroll
-  for (int c = 0; c < ROW_MAXC; ++c) {
-    int q = threadIdx.x + c * ROW_THREADS;
-    unpack16(buf_load16(din, (uint32_t)q * 16u), d[c], T());
-  }
   const int lane = threadIdx.x % MOE_WAVE, w = threadIdx.x / MOE_WAVE;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t rb = (uint32_t)rows[j] * row_bytes;
-    const float g = gates[j];
-    float part = 0.f;
+  // the token's dy row stays in registers (ROW_MAXC chunks per thread)
+  u32x4 draw[ROW_MAXC];
 #pragma unroll
-    for (int c = 0; c < ROW_MAXC; ++c) {
-      int q = threadIdx.x + c * ROW_THREADS;
-      if (q < nchunk) {
-        float tmp[VEC], o[VEC];
-        unpack16(buf_load16(ypr, rb + (uint32_t)q * 16u), tmp, T());
+  for (int c = 0; c < ROW_MAXC; ++c)
+    draw[c] = row_chunk(din, 0, threadIdx.x + c * ROW_THREADS, nchunk);
+  for (int j0 = 0; j0 < k; j0 += ROW_JB) {
+    float part[ROW_JB];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          part += d[c][i] * tmp[i];
-          o[i] = g * d[c][i];
+    for (int jj = 0; jj < ROW_JB; ++jj) part[jj] = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < ROW_MAXC; c0 += ROW_QB) {
+      if (c0 * ROW_THREADS >= nchunk) break;   // uniform
+      u32x4 v[ROW_JB][ROW_QB];
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u)
+            v[jj][u] = row_chunk(ypr, rb, threadIdx.x + (c0 + u) * ROW_THREADS, nchunk);
         }
-        buf_store16(dst, rb + (uint32_t)q * 16u, pack16(o, T()));
-      }
+#pragma unroll
+      for (int jj = 0; jj < ROW_JB; ++jj)
+        if (j0 + jj < k) {
+          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+          const float g = gates[j0 + jj];
+#pragma unroll
+          for (int u = 0; u < ROW_QB; ++u) {
+            const int q = threadIdx.x + (c0 + u) * ROW_THREADS;
+            float d[VEC], tmp[VEC], o[VEC];
+            unpack16(draw[c0 + u], d, T());
+            unpack16(v[jj][u], tmp, T());
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+              part[jj] += d[i] * tmp[i];
+              o[i] = g * d[i];
+            }
+            if (q < nchunk) buf_store16(dst, rb + (uint32_t)q * 16u, pack16(o, T()));
+          }
+        }
     }
-    part = wave_sum(part);
-    if (lane == 0) red[w] = part;
+#pragma unroll
+    for (int jj = 0; jj < ROW_JB; ++jj) {
+      const float ps = wave_sum(part[jj]);
+      if (lane == 0) red[jj][w] = ps;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float s = 0.f;
-      for (int i = 0; i < ROW_THREADS / MOE_WAVE; ++i) s += red[i];
-      dgate[(long long)t * k + j] = s;
+    if (threadIdx.x < ROW_JB && j0 + (int)threadIdx.x < k) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) sum += red[threadIdx.x][i];
+      dgate[(long long)t * k + j0 + threadIdx.x] = sum;
     }
     __syncthreads();
   }

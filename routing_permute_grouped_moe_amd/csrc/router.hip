@@ -200,14 +200,20 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 }
 
 // dbias: per-chunk column sums (256 tokens per chunk), then a fixed-order sum.
+#define COLSUM_ROWS 64   // rows of one column partial sum
 __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ dl, int T,
                                                           int E, float* __restrict__ part) {
   const int e = blockIdx.y * 256 + threadIdx.x;
   const int c = blockIdx.x;
   if (e >= E) return;
+  const int t0 = c * COLSUM_ROWS;
+  // all rows requested together, then added in row order
+  float v[COLSUM_ROWS];
+#pragma unroll
+  for (int i = 0; i < COLSUM_ROWS; ++i) v[i] = t0 + i < T ? dl[(long long)(t0 + i) * E + e] : 0.f;
   float s = 0.f;
-  const int t1 = min(T, (c + 1) * 256);
-  for (int t = c * 256; t < t1; ++t) s += dl[(long long)t * E + e];
+#pragma unroll
+  for (int i = 0; i < COLSUM_ROWS; ++i) s += v[i];
   part[(long long)c * E + e] = s;
 }
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part,
@@ -215,8 +221,15 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
                                                            float* __restrict__ out) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= E) return;
+  // partials requested 32 at a time, then added in chunk order (fp64)
   double s = 0.0;
-  for (int c = 0; c < nchunk; ++c) s += (double)part[(long long)c * E + e];
+  for (int c0 = 0; c0 < nchunk; c0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = c0 + i < nchunk ? part[(long long)(c0 + i) * E + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += (double)v[i];
+  }
   out[e] = (float)s;
 }
 
@@ -229,13 +242,12 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // workspace layout (bytes), forward and backward use it separately
 struct RouterWs {
-  size_t split, wg3s, wgb, part, dl3s, dlb, colpart, total;
+  size_t wg3s, wgb, part, dl3s, dlb, colpart, total;
 };
 static RouterWs router_ws_layout(int T, int H, int E) {
   RouterWs w = {};
   const size_t he = (size_t)H * E, te = (size_t)T * E;
   size_t o = 0;
-  w.split = o; o += align256(moe_gmm_split_ws_bytes());
   w.wg3s = o; o += align256(3 * he * 2);
   w.wgb = o; o += align256(he * 2);
   w.part = o;
@@ -243,7 +255,7 @@ static RouterWs router_ws_layout(int T, int H, int E) {
   o += align256(part_bytes);
   w.dl3s = o; o += align256(3 * te * 2);
   w.dlb = o; o += align256(te * 2);
-  w.colpart = o; o += align256((size_t)((T + 255) / 256) * E * 4);
+  w.colpart = o; o += align256((size_t)((T + COLSUM_ROWS - 1) / COLSUM_ROWS) * E * 4);
   w.total = o;
   return w;
 }
@@ -287,7 +299,7 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
     hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
                        wg3s, (bf16_t*)nullptr);
     MOE_TRY(moe_check_launch(fn));
-    MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, w + L.split, s));
+    MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, s));
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s,
                        (const float*)part, (long long)T * E, E, bias, logits);
     return moe_check_launch(fn);
@@ -332,7 +344,7 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
                         need);
     }
   }
-  const int nchunk = (T + 255) / 256;
+  const int nchunk = (T + COLSUM_ROWS - 1) / COLSUM_ROWS;
   if (mfma) {
     char* w = (char*)ws;
     bf16_t* wg3s = (bf16_t*)(w + L.wg3s);
@@ -346,8 +358,8 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
     hipLaunchKernelGGL(split_dl_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s, dlogits,
                        T, E, dl3s, dlb);
     MOE_TRY(moe_check_launch(fn));
-    MOE_TRY(moe_gmm_router_dx(dlb, wgb, dx, T, H, E, w + L.split, s));
-    MOE_TRY(moe_gmm_router_dwg(x, dl3s, part, T, H, E, RT_SPLIT, w + L.split, s));
+    MOE_TRY(moe_gmm_router_dx(dlb, wgb, dx, T, H, E, s));
+    MOE_TRY(moe_gmm_router_dwg(x, dl3s, part, T, H, E, RT_SPLIT, s));
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s,
                        (const float*)part, (long long)H * E, E, (const float*)nullptr, dwg);
     MOE_TRY(moe_check_launch(fn));
