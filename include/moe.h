@@ -171,12 +171,14 @@ int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row
  * Arithmetic: dt products, fp32 accumulation; outputs stored as dt.
  *
  * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes, 256-byte
- * aligned, contents scratch.  With it the K steps of all tiles are spread
- * evenly over the workgroups and a tile cut between two of them is finished
- * by the last to arrive, which adds the fp32 partial tiles in a fixed order
- * (results stay bitwise reproducible).  With ws == NULL every tile is
- * computed whole by one workgroup (same results up to fp32 summation order).
- * Calls that share one workspace must not run concurrently.
+ * aligned, holding the tile scheduler's counters.  It must be zero-filled
+ * before its first use; every call returns it to zero when it completes.
+ * With it, the workgroups of each XCD take their tiles from a shared counter
+ * (a workgroup that starts late, e.g. while another kernel still holds its
+ * CU, just takes fewer tiles); with ws == NULL they take a fixed share.
+ * Results are identical either way (each tile is computed whole, in the same
+ * order, by one workgroup).  Calls that run concurrently (on different
+ * streams) need separate workspaces.
  */
 size_t moe_gmm_workspace_bytes(void);
 typedef struct moe_shared_expert {

@@ -48,7 +48,6 @@ constexpr int RING_BYTES = 131072;   // LDS ring of operand stages (also the epi
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
 constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
 constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer range
-constexpr int CPOL_SYS = 1 | 16;       // cache policy sc0 | sc1: system-coherent access
 
 enum Mode { FWD1 = 0, FWD2 = 1, DX1 = 2, DX2 = 3, DW = 4 };
 
@@ -70,9 +69,9 @@ struct GmmArgs {
   int dense; long long x_gs;
   int kwrap;     // > 0: the A operand's K index wraps with this period
   int out_f32;   // plain-store epilogue writes fp32 whatever T is
-  // split-tile workspace (NULL: every tile is computed whole by one workgroup)
-  int* cnt;      // one arrival counter per workgroup, zero on entry
-  float* part;   // 2 partial tiles (256 x 256 fp32) per workgroup
+  // tile scheduler counters (NULL: static tile order): 8 per-XCD tile
+  // counters and a finished-workgroup counter, zero on entry and on exit
+  int* cnt;
 };
 
 // Per element type: K step BK (KS MFMA k-steps), ring of STAGES stages of two
@@ -315,7 +314,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
   __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
   __shared__ int g_kp[MOE_MAX_E + 2];   // DW: K steps before each group in work order
-  __shared__ int s_last;
+  __shared__ int s_next;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -406,61 +405,48 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     __syncthreads();
   }
 
-  // ---- persistent loop, XCD-aware workgroup numbering.  Whole tiles are
-  // dealt round-robin, so the workgroups in flight work on neighbouring tiles
-  // and share their operand panels in L2.  With a workspace, the tiles of the
-  // last one-to-two rounds (which would leave part of the chip idle) are
-  // instead cut along K: their K steps form one sequence split into equal
-  // contiguous ranges, one per workgroup; a tile cut by a range boundary is
-  // finished by the last of its workgroups to arrive, which adds the fp32
-  // partial tiles in workgroup order (deterministic) and runs the epilogue.
+  // ---- persistent loop over tiles.  Tiles are dealt in rounds of one per
+  // workgroup; in each round the workgroups of XCD x (workgroup i runs on XCD
+  // i % 8) take the round's x-th block of consecutive tiles, so an XCD's
+  // workgroups share operand panels in its L2 and the whole chip works on one
+  // compact stretch of tiles at a time (whose operands stay in the MALL).
+  // Without a workspace workgroup w of an XCD takes the w-th tile of each of
+  // its blocks; with one the XCD's workgroups draw its tiles in order from the
+  // XCD's counter, so a workgroup that starts late (its CU was still busy
+  // with another kernel) or drew short tiles just takes fewer or more.
   const int nwg = gridDim.x;
   const int bid = blockIdx.x;
-  const int L = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-  const int KTm = (a.K + BK - 1) / BK;   // K steps of an M-var tile
+  const int nx = (nwg % 8 == 0) ? 8 : 1;
+  const int xcd = bid % nx, wpx = nwg / nx, wix = bid / nx;
   const int per = MBt * NBt;             // DW: tiles of one group
-  // first K step of tile t in the sequence of all tiles' K steps
-  auto kstart = [&](int t) -> long long {
-    if constexpr (MODE != DW) {
-      return (long long)t * KTm;
-    } else {
-      if (t >= total) return g_kp[ng];
-      const int p = t / per;
-      const int gg = g_pre[p];
-      return g_kp[p] + (long long)(t % per) * max(1, (g_hi[gg] - g_lo[gg] + BK - 1) / BK);
-    }
-  };
-  // The K cut pays only when the last round of whole tiles would leave most
-  // workgroups idle (fewer than half of them busy); otherwise the partial
-  // tiles' extra traffic costs more than the idle time it removes.
-  const int rounds = total / nwg, rem = total % nwg;
-  const int dp_tiles =
-      (a.part != nullptr && rounds >= 1 && rem != 0 && 2 * rem < nwg) ? (rounds - 1) * nwg : total;
-  const long long k0 = uniform(kstart(dp_tiles));
-  const long long W = uniform(kstart(total)) - k0;   // K steps of the cut region
-  // K steps of the region's longest tile (its first one: M-var tiles are all
-  // alike, dW tiles come in descending order of their K steps).  Ranges are
-  // at least that long, so a boundary falls inside a tile at most once:
-  // every cut tile has exactly two partial sums, and their fp32 sum does not
-  // depend on which of the two workgroups adds them (deterministic result).
-  const long long kmax = dp_tiles < total ? uniform(kstart(dp_tiles + 1)) - k0 : 1;
-  const int nsh = (int)min((long long)nwg, W / kmax);
-  const bool active = L < nsh;
-  const long long r_beg = active ? k0 + W * L / nsh : 0;
-  const long long r_end = active ? k0 + W * (L + 1) / nsh : 0;
-  auto wg_of = [&](long long k) { return (int)(((k - k0 + 1) * nsh - 1) / W); };
+  // n-th tile of this XCD's sequence
+  auto tile_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
+  int* const ctr = a.cnt;   // [0, 8): per-XCD tile counters, [8]: finished workgroups
+  const bool dyn = ctr != nullptr;
+  int k = wix;              // index of this workgroup's tile inside the chunk
+  int grab = 0;             // thread 0: the counter value drawn during the last epilogue
 
-  long long cur = r_beg;
-  int rr_tile = L;
-  while (rr_tile < dp_tiles || cur < r_end) {
-    const bool split = rr_tile >= dp_tiles;
-    // ---- locate the round-robin tile or the tile holding K step cur
-    int tile, g, m0, n0, rows0 = 0, rows = 0, kdim, KTe;
-    long long t_start;
+  for (bool first = true;; first = false) {
+    // every wave is done reading the ring (previous tile), the previous
+    // tile's stores have left, and the tile draw has returned
+    wait_vm<0>();
+    __syncthreads();
+    if (!first) {
+      if (dyn) {
+        if (tid == 0) s_next = wpx + grab;
+        __syncthreads();
+        k = s_next;
+      } else {
+        k += wpx;
+      }
+    }
+    k = uniform(k);
+    const int tile_id = tile_of(k);
+    if (tile_id >= total) break;
+    // ---- locate the tile
+    int g, m0, n0, rows0 = 0, rows = 0, kdim;
     if constexpr (MODE != DW) {
-      tile = split ? (int)(cur / KTm) : rr_tile;
-      KTe = KTm;
-      t_start = (long long)tile * KTm;
+      const int tile = tile_id;
       const int MT = g_pre[ng];
       const int band = GM_BAND * NBt;
       const int sup = tile / band, within = tile % band;
@@ -481,26 +467,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       n0 = nbi * ((MODE == FWD1) ? BN / 2 : BN);
       kdim = a.K;
     } else {
-      int p, local;
-      if (split) {
-        int lo = 0, hi = ng - 1;   // last work position with g_kp[p] <= cur
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (g_kp[mid] <= cur) lo = mid; else hi = mid - 1;
-        }
-        p = lo;
-        g = g_pre[p];
-        KTe = max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
-        local = (int)((cur - g_kp[p]) / KTe);
-        t_start = g_kp[p] + (long long)local * KTe;
-      } else {
-        p = rr_tile / per;
-        local = rr_tile % per;
-        g = g_pre[p];
-        KTe = max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
-        t_start = 0;
-      }
-      tile = p * per + local;
+      const int p = tile_id / per, local = tile_id % per;
+      g = g_pre[p];
       const int band = GM_BAND * NBt;
       const int sup = local / band, within = local % band;
       const int first = sup * GM_BAND;
@@ -510,12 +478,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       rows0 = g_lo[g];
       kdim = g_hi[g] - g_lo[g];
     }
-    // K steps [s0, s1) of this tile belong to this workgroup
-    const int s0 = split ? (int)(cur - t_start) : 0;
-    const int s1 = split ? (int)min((long long)KTe, r_end - t_start) : KTe;
-    const bool whole = (s0 == 0 && s1 == KTe);
-    if (split) cur = t_start + s1; else rr_tile += nwg;
-    t_start = uniform(t_start); KTe = uniform(KTe);
     g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
     rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
     const bool sh = g >= a.G;
@@ -549,9 +511,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int KTr = (kdim + BK - 1) / BK;            // K steps with data
-    const int kb = min(s0, KTr), ke = min(s1, KTr);  // this workgroup's steps
-    const int KT = ke - kb;
+    const int KT = (kdim + BK - 1) / BK;   // K steps with data
     uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
     if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
     else kmajor_offsets<T, false>(va, m0, 0, offa);
@@ -560,11 +520,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
     const int sb = B_MN ? vb.ld * BK * ES : BK * ES;
     const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
-    auto issue = [&](int kt) {   // kt counts from kb
+    auto issue = [&](int kt) {
       const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-      const int kg = kb + kt;
-      issue_op(va, st, offa, (kg % wrap_steps) * sa);
-      issue_op(vb, st + OPB, offb, kg * sb);
+      issue_op(va, st, offa, (kt % wrap_steps) * sa);
+      issue_op(vb, st + OPB, offb, kt * sb);
     };
     // copy j of K step kt (j < DMA_PER_OP: operand A, else B); a step past the
     // last one copies through an empty descriptor, which moves no HBM bytes
@@ -572,8 +531,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
     const uint32_t lds_w = lds_addr(smem) + (threadIdx.x >> 6) * DMA_PER_OP * 1024;
     // (the A step index wraps for dW tiles that re-read a short operand;
-    // ka_next tracks (kb + kt) % wrap_steps of the next step to issue)
-    int ka_next = kb % wrap_steps;
+    // ka_next tracks kt % wrap_steps of the next step to issue)
+    int ka_next = 0;
     auto issue1 = [&](int kt, int j) {
       const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
       const bool live = kt < KT;
@@ -581,26 +540,20 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         dma16(live ? va.rs : rs_none, st + j * 1024, offa[j], ka_next * sa);
       else
         dma16(live ? vb.rs : rs_none, st + OPB + (j - DMA_PER_OP) * 1024, offb[j - DMA_PER_OP],
-              (kb + kt) * sb);
+              kt * sb);
       if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
     };
     auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
 
-    // every wave must be done reading the ring (previous tile) and its
-    // epilogue stores must have left before the ring is refilled
-    wait_vm<0>();
-    __syncthreads();
     if (KT > 0) {
       if constexpr (sizeof(T) == 2) {
-        // steps 0 and 1 and the A copies of step 2 in flight (empty copies
-        // past the end), so the wait counts below hold for every K step
+        // steps 0, 1 and 2 in flight (empty copies past the end), so the
+        // wait counts below hold for every K step
 #pragma unroll
-        for (int kt = 0; kt < STAGES - 2; ++kt)
+        for (int kt = 0; kt < STAGES - 1; ++kt)
 #pragma unroll
           for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
-#pragma unroll
-        for (int j = 0; j < DMA_PER_OP; ++j) issue1(STAGES - 2, j);
-        wait_vm<DMA_PER_STEP + DMA_PER_OP>();
+        wait_vm<2 * DMA_PER_STEP>();
       } else {
         for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
         if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
@@ -613,11 +566,12 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         // the other work woven between them (pinned by scheduling barriers),
         // so the matrix pipe never waits on a burst of LDS reads or copy
         // issues: the first half loads the second half's fragments and issues
-        // the B copies of step kt+2; the second half (after the barrier)
-        // loads the first half fragments of step kt+1 and issues the A copies
-        // of step kt+3 (a stage is free from the barrier after its last read,
-        // and splitting a step's copies over two halves measured ~10% fewer
-        // cycles per step than issuing them together).  Steps past the end
+        // the A copies of step kt+3; the second half (after the barrier)
+        // loads the first half fragments of step kt+1 and issues the B copies
+        // of step kt+3 (step kt+3's stage held step kt-1, whose last reads
+        // retired at the previous barrier; splitting a step's copies over two
+        // halves measured ~10% fewer cycles per step than issuing them
+        // together).  Steps past the end
         // copy through the empty descriptor, so every step looks the same.
         Frags<T, A_MN, B_MN> f0, f1;
         f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
@@ -632,14 +586,14 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
               if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-              else if (q - (FM + FN) < DMA_PER_OP)
-                issue1(kt + STAGES - 2, DMA_PER_OP + q - (FM + FN));
+              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
               __builtin_amdgcn_sched_barrier(0);
             }
-          // K step kt+1 has landed once at most one later step of this wave's
-          // copies is outstanding; the barrier extends that to all waves and
-          // retires every read of the stage refilled next
-          wait_vm<DMA_PER_STEP>();
+          // K step kt+1 has landed once at most the copies issued after it
+          // (step kt+2, and step kt+3's A copies) are outstanding; the
+          // barrier extends that to all waves and retires every read of the
+          // stage refilled next
+          wait_vm<DMA_PER_STEP + DMA_PER_OP>();
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -649,7 +603,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
               if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
+              else if (q - (FM + FN) < DMA_PER_OP)
+                issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
               __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -680,54 +635,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
     // every HBM access is a 16-byte row chunk.  Slice s holds fragments 2s and
     // 2s+1 of every wave (FWD1: s = 0 gate, s = 1 up columns).
-    // ---- a cut tile: both workgroups on it park their fp32 partial tile in
-    // the accumulator layout (each lane's 64 16-byte chunks, coalesced); the
-    // second to arrive goes on to the epilogue, which adds the other's partial
-    // chunk by chunk as it stages the accumulators, and the first moves on to
-    // its next tile.
-    constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
-    auto chunk_off = [&](int i, int j, int q) {
-      return (uint32_t)((((i * FN + j) * 4 + q) * NT + (int)threadIdx.x) * 16);
-    };
-    __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, 0);   // partner's partial tile
-    const bool fix = !whole;
-    if (!whole) {
-      const int w_first = wg_of(t_start);   // range holding the tile's first step
-      const int which = (r_beg >= t_start) ? 0 : 1;   // first or last tile of the range
-      const __amdgpu_buffer_rsrc_t pw =
-          make_rsrc((const char*)a.part + (long long)(2 * L + which) * SLOT, SLOT);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                             acc[i][j][4 * q + 3]};
-            // system-coherent (sc0 sc1) stores: visible to the other XCDs'
-            // L2s without writing back or invalidating whole caches
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pw,
-                                                   chunk_off(i, j, q), 0, CPOL_SYS);
-          }
-        __builtin_amdgcn_sched_barrier(0);   // a few accumulators out at a time
-      }
-      wait_vm<0>();   // this wave's partial stores have completed
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(a.cnt + w_first, 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old == 1;
-        if (last) __hip_atomic_store(a.cnt + w_first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last ? 1 : 0;
-      }
-      __syncthreads();
-      if (!s_last) continue;
-      // the other workgroup and the slot it parked this tile in
-      const int partner = (L == w_first) ? w_first + 1 : w_first;
-      const int ph = (k0 + W * partner / nsh >= t_start) ? 0 : 1;
-      pr = make_rsrc((const char*)a.part + (long long)(2 * partner + ph) * SLOT, SLOT);
-    }
-
     // a per-tile copy of the thread index: the epilogue's address arithmetic
     // then belongs to this tile and is not kept live (and spilled) across
     // the persistent loop as an invariant
@@ -736,11 +643,11 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const int elane = etid & 63;
     wait_vm<0>();      // the empty copies past the last step have landed
     __syncthreads();   // every wave is done with the ring
+    // draw the next tile now: the atomic's latency hides behind the epilogue
+    // (its value is read after the next iteration's full wait)
+    if (dyn && tid == 0)
+      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float* ep = (float*)smem;
-    auto partner_chunk = [&](int f, int fn, int rq) {
-      return __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, chunk_off(f, fn, rq), 0, CPOL_SYS));
-    };
     auto put = [&](auto fn0c, auto&& value) {
       // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
       // (fn0 is a compile-time constant so the accumulators stay in registers);
@@ -765,30 +672,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           }
       __syncthreads();
     };
-    // a cut tile: add the other workgroup's partial of fragments fn0, fn0+1
-    // to the staged slice (each lane updates the words it put)
-    auto add_partner = [&](auto fn0c) {
-      if (!fix) return;
-      constexpr int slice_fn0 = decltype(fn0c)::value;
-      const int m = elane & 31;
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        f32x4 pv[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) pv[j][rq] = partner_chunk(f, slice_fn0 + j, rq);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int row = wm * WTM + f * 32 + m;
-            const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
-            *(f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2)) += pv[j][rq];
-          }
-      }
-      __syncthreads();
-    };
     auto take = [&](auto&& consume) {
       // 256 rows x 16 chunks of 8 columns, 16 per thread
 #pragma unroll 4
@@ -811,7 +694,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     auto emit = [&](auto slc, auto&& consume) {
       constexpr int sl = decltype(slc)::value;
       put(std::integral_constant<int, 2 * sl>{}, acc_of);
-      add_partner(std::integral_constant<int, 2 * sl>{});
       take(consume);
     };
 
@@ -853,7 +735,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       // elane rewrites the very words it put, so no barrier in between and
       // the gate accumulators are dead once the slice is staged); up last
       put(std::integral_constant<int, 0>{}, acc_of);
-      add_partner(std::integral_constant<int, 0>{});
       take(store_gate);
       {
         const int m = elane & 31;
@@ -867,9 +748,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
               f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
               f32x4 v = *pp;
-              f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
-                         acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
-              if (fix) u += partner_chunk(f, 2 + j, rq);
+              const f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
+                               acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
               v.x = v.x * sigmoidf_(v.x) * u.x;
               v.y = v.y * sigmoidf_(v.y) * u.y;
               v.z = v.z * sigmoidf_(v.z) * u.z;
@@ -880,7 +760,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       }
       take(store_act);
       put(std::integral_constant<int, 2>{}, acc_of);
-      add_partner(std::integral_constant<int, 2>{});
       take(store_up);
     } else {
       // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
@@ -940,7 +819,6 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 #pragma unroll
             for (int it = 0; it < 8; ++it) fetch(it);
             put(std::integral_constant<int, 2 * h>{}, acc_of);
-            add_partner(std::integral_constant<int, 2 * h>{});
 #pragma unroll
             for (int it = 8; it < 16; ++it) fetch(it);
 #pragma unroll
@@ -994,13 +872,17 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       slice(std::integral_constant<int, 1>{});
     }
   }
+  // every draw of this workgroup has returned (the last one ended the loop);
+  // the last workgroup to finish returns the counters to zero for the next call
+  if (dyn && tid == 0) {
+    const int done = __hip_atomic_fetch_add(ctr + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == nwg - 1)
+      for (int i = 0; i <= 8; ++i)
+        __hip_atomic_store(ctr + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------- host side
-
-__global__ void zero_counters_kernel(int* cnt, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = 0;
-}
 
 int grid_size() {
   const int n = moe_cu_count();
@@ -1009,13 +891,7 @@ int grid_size() {
 
 template <typename T, int MODE>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
-  const int grid = grid_size();
-  if (a.cnt) {
-    // counters must start at zero (a fill kernel, safe inside graph capture)
-    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(256), 0, s, a.cnt, grid);
-    MOE_TRY(moe_check_launch(what));
-  }
-  hipLaunchKernelGGL((gmm_kernel<T, MODE>), dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gmm_kernel<T, MODE>), dim3(grid_size()), dim3(NT), 0, s, a);
   return moe_check_launch(what);
 }
 
@@ -1048,19 +924,16 @@ int gmm_checks(const char* fn, const int32_t* offsets, int g0, int G, int R, int
   return MOE_OK;
 }
 
-constexpr size_t WS_CNT_BYTES = 4096;   // counters (<= 1024 workgroups)
+constexpr size_t WS_BYTES = 256;   // 9 scheduler counters, padded
 
-size_t ws_bytes_needed() { return WS_CNT_BYTES + (size_t)2 * grid_size() * BM * BN * 4; }
-
-// Attach a split-tile workspace (NULL: whole tiles only).
+// Attach the scheduler workspace (NULL: static tile order).
 int attach_ws(GmmArgs& a, void* ws, size_t ws_bytes, const char* fn) {
   if (ws == nullptr) return MOE_OK;
   MOE_TRY(moe_need_ptr(ws, fn, "ws", 256));
-  if (ws_bytes < ws_bytes_needed())
+  if (ws_bytes < WS_BYTES)
     return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
-                    ws_bytes_needed());
+                    WS_BYTES);
   a.cnt = (int*)ws;
-  a.part = (float*)((char*)ws + WS_CNT_BYTES);
   return MOE_OK;
 }
 
@@ -1077,7 +950,7 @@ GmmArgs base_args(const int32_t* offsets, int g0, int G, int R, const moe_shared
 
 }  // namespace
 
-extern "C" size_t moe_gmm_workspace_bytes(void) { return ws_bytes_needed(); }
+extern "C" size_t moe_gmm_workspace_bytes(void) { return WS_BYTES; }
 
 extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
                                     int dt, int H, int I, const void* w13, const void* w2,

@@ -10,6 +10,13 @@ Backward: combine bwd -> grouped GEMM dX -> grouped GEMM dW -> route bwd ->
           router bwd -> permute bwd (which also adds the shared expert's and
           the router's input gradients).
 
+With ``overlap`` (the default on a GPU) the work that does not depend on the
+routing runs on a second stream of the same priority: the shared expert's
+GEMMs (forward and backward) and the router backward.  The grouped GEMM draws
+its tiles from per-XCD counters, so whichever kernel holds fewer CUs at the
+end of another one's last round simply takes fewer tiles; results are
+bitwise identical to the sequential order.
+
 Experts outside ``[g0, g0+G)`` are remote: their rows are moved by the
 permute and the combine, their expert outputs and input gradients are zero
 (the buffers are cleared once at allocation and never written), and they get
@@ -50,8 +57,9 @@ class LayerShape:
 class MoeLayer:
     """Device buffers of one layer plus the forward/backward call sequences."""
 
-    def __init__(self, shape: LayerShape, device="cuda"):
+    def __init__(self, shape: LayerShape, device="cuda", overlap: bool = True):
         s = self.s = shape
+        self.overlap = overlap
         dev = self.device = torch.device(device)
         dt, f32, i32 = s.dtype, torch.float32, torch.int32
         self.dt = abi.MOE_BF16 if dt == torch.bfloat16 else abi.MOE_F32
@@ -80,10 +88,13 @@ class MoeLayer:
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         self.rws_bytes = abi.moe_router_workspace_bytes(T, H, E, self.dt) if s.router else 0
         self.rws = torch.empty(max(self.rws_bytes, 256), dtype=torch.uint8, device=dev)
-        # K-split workspace of the grouped GEMM: off by default (whole tiles
-        # measure faster on the shapes here); enable_gemm_split() turns it on
-        self.gws_bytes = 0
-        self.gws = None
+        # tile scheduler counters of the grouped GEMM (zero-filled once; every
+        # call leaves them zero); set_gemm_dynamic(False) selects the static order
+        self.gws_bytes = abi.moe_gmm_workspace_bytes()
+        self.gws = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=dev)
+        self.gws_aux = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=dev)
+        self.aux = torch.cuda.Stream(device=dev) if overlap else None
+        self._ev = [torch.cuda.Event() for _ in range(4)] if overlap else None
         self.h13 = e(R, 2 * I)
         self.act = e(R, I)
         self.yp = z(R, H)            # remote rows stay zero
@@ -112,13 +123,14 @@ class MoeLayer:
             self.dws2 = e(H, I)
 
     # ------------------------------------------------------------------ helpers
-    def enable_gemm_split(self, on: bool = True):
-        """Let the grouped GEMM cut the tiles of its last rounds along K."""
+    def set_gemm_dynamic(self, on: bool = True):
+        """Grouped GEMM tiles from per-XCD counters (True) or a fixed share (False)."""
         if on:
             self.gws_bytes = abi.moe_gmm_workspace_bytes()
-            self.gws = torch.empty(self.gws_bytes, dtype=torch.uint8, device=self.device)
+            self.gws = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=self.device)
+            self.gws_aux = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=self.device)
         else:
-            self.gws_bytes, self.gws = 0, None
+            self.gws_bytes, self.gws, self.gws_aux = 0, None, None
 
     def shared_desc(self):
         if not self.s.shared:
@@ -144,11 +156,21 @@ class MoeLayer:
                         self.offsets, self.row_id_map, self.src_token, self.ws, self.ws_bytes,
                         stream)
 
-    def gmm_fwd(self, stream=None, shared=None):
+    def _gmm_sel(self, part):
+        """(G, shared descriptor, workspace) of one grouped-GEMM launch set:
+        part = "all" (routed + shared), "routed" or "shared"."""
         s = self.s
-        sh = self.shared_desc() if shared is None else shared
-        abi.moe_grouped_gemm_fwd(self.xp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H, s.I,
-                                 self.w13, self.w2, self.h13, self.act, self.yp, sh, self.gws,
+        if part == "shared":
+            return 0, self.shared_desc(), self.gws_aux
+        if part == "routed":
+            return s.groups, None, self.gws
+        return s.groups, self.shared_desc(), self.gws
+
+    def gmm_fwd(self, stream=None, part="all"):
+        s = self.s
+        G, sh, ws = self._gmm_sel(part)
+        abi.moe_grouped_gemm_fwd(self.xp, self.offsets, s.g0, G, s.R, self.dt, s.H, s.I,
+                                 self.w13, self.w2, self.h13, self.act, self.yp, sh, ws,
                                  self.gws_bytes, stream)
 
     def combine(self, stream=None):
@@ -162,19 +184,19 @@ class MoeLayer:
         abi.moe_unpermute_combine_bwd(self.dy, self.yp, self.row_id_map, self.gate, self.dt, s.T,
                                       s.H, s.k, self.dyp, self.dgate, stream)
 
-    def gmm_bwd_dx(self, stream=None, shared=None):
+    def gmm_bwd_dx(self, stream=None, part="all"):
         s = self.s
-        sh = self.shared_desc() if shared is None else shared
-        abi.moe_grouped_gemm_bwd_dx(self.dyp, self.offsets, s.g0, s.groups, s.R, self.dt, s.H,
-                                    s.I, self.w13, self.w2, self.h13, self.dh13, self.dxp, sh,
-                                    self.gws, self.gws_bytes, stream)
+        G, sh, ws = self._gmm_sel(part)
+        abi.moe_grouped_gemm_bwd_dx(self.dyp, self.offsets, s.g0, G, s.R, self.dt, s.H, s.I,
+                                    self.w13, self.w2, self.h13, self.dh13, self.dxp, sh, ws,
+                                    self.gws_bytes, stream)
 
-    def gmm_bwd_dw(self, stream=None, shared=None):
+    def gmm_bwd_dw(self, stream=None, part="all"):
         s = self.s
-        sh = self.shared_desc() if shared is None else shared
+        G, sh, ws = self._gmm_sel(part)
         abi.moe_grouped_gemm_bwd_dw(self.xp, self.act, self.dyp, self.dh13, self.offsets, s.g0,
-                                    s.groups, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh,
-                                    self.gws, self.gws_bytes, stream)
+                                    G, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh, ws,
+                                    self.gws_bytes, stream)
 
     def route_bwd(self, stream=None):
         s = self.s
@@ -193,8 +215,28 @@ class MoeLayer:
                             self.dx_router if s.router else None, self.dx, stream)
 
     # ------------------------------------------------------------------ passes
+    def _streams(self, stream):
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        return main, self.aux
+
     def forward(self, stream=None):
-        if self.s.router:
+        s = self.s
+        if self.overlap and s.shared:
+            main, aux = self._streams(stream)
+            ev_in, ev_sh = self._ev[0], self._ev[1]
+            ev_in.record(main)
+            aux.wait_event(ev_in)
+            self.gmm_fwd(aux, part="shared")            # needs x only
+            ev_sh.record(aux)
+            if s.router:
+                self.router_fwd(main)
+            self.route(main)
+            self.permute(main)
+            self.gmm_fwd(main, part="routed")
+            main.wait_event(ev_sh)
+            self.combine(main)
+            return
+        if s.router:
             self.router_fwd(stream)
         self.route(stream)
         self.permute(stream)
@@ -202,11 +244,33 @@ class MoeLayer:
         self.combine(stream)
 
     def backward(self, stream=None):
+        s = self.s
+        if self.overlap and (s.shared or s.router):
+            main, aux = self._streams(stream)
+            ev_in, ev_c, ev_aux = self._ev[0], self._ev[2], self._ev[3]
+            ev_in.record(main)
+            aux.wait_event(ev_in)
+            if s.shared:                                # needs dy and the forward's saves
+                self.gmm_bwd_dx(aux, part="shared")
+                self.gmm_bwd_dw(aux, part="shared")
+            self.combine_bwd(main)
+            ev_c.record(main)
+            aux.wait_event(ev_c)
+            self.route_bwd(aux)                         # needs dgate
+            if s.router:
+                self.router_bwd(aux)
+            ev_aux.record(aux)
+            routed = "routed" if s.shared else "all"
+            self.gmm_bwd_dx(main, part=routed)
+            self.gmm_bwd_dw(main, part=routed)
+            main.wait_event(ev_aux)
+            self.permute_bwd(main)
+            return
         self.combine_bwd(stream)
         self.gmm_bwd_dx(stream)
         self.gmm_bwd_dw(stream)
         self.route_bwd(stream)
-        if self.s.router:
+        if s.router:
             self.router_bwd(stream)
         self.permute_bwd(stream)
 

@@ -108,7 +108,7 @@ def test_shape_limits(abi):
                 FAKE, FAKE, FAKE, None, None, 0, None)
     # a workspace that is too small
     st2 = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 0, 8, 64, 1, 128, 64, FAKE, FAKE, FAKE,
-                 FAKE, FAKE, None, FAKE, 4096, None)
+                 FAKE, FAKE, None, FAKE, 16, None)
     assert st2 == abi.MOE_ERR_WORKSPACE
     assert st == abi.MOE_ERR_UNSUPPORTED
     # a row longer than the row kernels keep in registers

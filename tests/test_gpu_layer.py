@@ -27,13 +27,13 @@ def near_tie_tokens(logits, k):
     return (s[:, k - 1] - s[:, k]) < 1e-5
 
 
-def check_layer(name, split=False, **overrides):
+def check_layer(name, dynamic=True, overlap=True, **overrides):
     cfg = synth.get_config(name, **overrides)
     print(f"\n[layer] config={cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
-          f"gemm_split={split}", flush=True)
+          f"gemm_dynamic={dynamic} overlap={overlap}", flush=True)
     inp = synth.make_inputs(cfg)
-    L = make_layer(cfg, inp)
-    L.enable_gemm_split(split)
+    L = make_layer(cfg, inp, overlap=overlap)
+    L.set_gemm_dynamic(dynamic)
     L.forward()
     L.backward()
     torch.cuda.synchronize()
@@ -106,10 +106,30 @@ def test_layer_pangu_share_full_size():
     check_layer("pangu")
 
 
-def test_layer_pangu_share_full_size_gemm_split():
-    # the grouped GEMM with K-cut tail tiles (fp32 partial tiles summed in a
-    # fixed order by the last workgroup to arrive)
-    check_layer("pangu", split=True)
+def test_layer_pangu_share_full_size_static_tiles():
+    # the grouped GEMM with its static tile order (no scheduler workspace),
+    # every call on one stream
+    check_layer("pangu", dynamic=False, overlap=False)
+
+
+def test_layer_overlap_matches_sequential_bitwise():
+    # shared expert and router backward on the second stream: same bits as
+    # the one-stream order, over two steps in a row
+    cfg = synth.get_config("pangu")
+    inp = synth.make_inputs(cfg)
+    L = make_layer(cfg, inp)
+    names = ("y", "dx", "dw13", "dw2", "dwg", "dbias", "dws13", "dws2", "dgate")
+    res = {}
+    for ov in (False, True, True):
+        L.overlap = ov
+        L.step()
+        torch.cuda.synchronize()
+        got = [getattr(L, n).clone() for n in names]
+        if ov in res:
+            assert all(torch.equal(a, b) for a, b in zip(res[ov], got))
+        res[ov] = got
+    for n, a, b in zip(names, res[False], res[True]):
+        assert torch.equal(a, b), n
 
 
 def test_layer_deepseek_shape_reduced_width():
@@ -123,12 +143,12 @@ def test_layer_stress_shape_reduced_width():
     check_layer("stress", H=512)
 
 
-@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
-def test_layer_step_is_bitwise_deterministic(split):
+@pytest.mark.parametrize("dynamic", [False, True], ids=["static", "dynamic"])
+def test_layer_step_is_bitwise_deterministic(dynamic):
     cfg = synth.get_config("small", T=1024)
     inp = synth.make_inputs(cfg)
     L = make_layer(cfg, inp)
-    L.enable_gemm_split(split)
+    L.set_gemm_dynamic(dynamic)
     outs = []
     for _ in range(2):
         L.step()
