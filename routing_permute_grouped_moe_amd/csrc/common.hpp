@@ -22,12 +22,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// IEEE round-to-nearest-even of fp32 to bf16 (NaN stays NaN).
+// IEEE round-to-nearest-even of fp32 to bf16 (NaN stays NaN): gfx950's
+// hardware conversion, branch-free (a software version with a NaN test
+// compiles to divergent branches per element).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 template <typename T> struct Elem;

@@ -47,7 +47,14 @@ constexpr int FM = 4, FN = 4;        // 32x32 fragments per wave tile
 constexpr int RING_BYTES = 131072;   // LDS ring of operand stages (also the epilogue slice)
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
 constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
-constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer range
+constexpr uint32_t OOB = 0x80000000u;  // byte offset past every operand range (loads)
+// Byte offset of a dropped store: past every output range, whose descriptor
+// sizes are capped by out_bytes(); the epilogues compute a store's offset
+// with this in place of a branch, so they stay free of divergent control flow.
+constexpr uint32_t DROP = 0xFFFFFFF0u;
+__host__ __device__ __forceinline__ uint32_t out_bytes(long long b) {
+  return b <= 0 ? 0u : (b >= 0xFFFFFFE0LL ? 0xFFFFFFE0u : (uint32_t)b);
+}
 
 enum Mode { FWD1 = 0, FWD2 = 1, DX1 = 2, DX2 = 3, DW = 4 };
 
@@ -697,20 +704,22 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       take(consume);
     };
 
-    auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, const float* v) {
+    // 8 values at element elem of an output (dropped unless ok)
+    auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, const float* v) {
       if constexpr (sizeof(T) == 2) {
-        buf_store16(rs, elem * 2u, pack16(v, T()));
+        buf_store16(rs, ok ? elem * 2u : DROP, pack16(v, T()));
       } else {
-        buf_store16(rs, elem * 4u, pack16(v, T()));
-        buf_store16(rs, elem * 4u + 16u, pack16(v + 4, T()));
+        buf_store16(rs, ok ? elem * 4u : DROP, pack16(v, T()));
+        buf_store16(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
       }
     };
-    auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t elem, float* v) {
+    // 8 values at element elem of an operand (zeros unless ok)
+    auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, float* v) {
       if constexpr (sizeof(T) == 2) {
-        unpack16(buf_load16(rs, elem * 2u), v, T());
+        unpack16(buf_load16(rs, ok ? elem * 2u : OOB), v, T());
       } else {
-        unpack16(buf_load16(rs, elem * 4u), v, T());
-        unpack16(buf_load16(rs, elem * 4u + 16u), v + 4, T());
+        unpack16(buf_load16(rs, ok ? elem * 4u : OOB), v, T());
+        unpack16(buf_load16(rs, ok ? elem * 4u + 16u : OOB), v + 4, T());
       }
     };
     if constexpr (MODE == FWD1) {
@@ -719,17 +728,17 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       void* hb = sh ? a.sC : a.C;
       void* ab = sh ? a.sC2 : a.C2;
       const __amdgpu_buffer_rsrc_t hr = make_rsrc((char*)hb + (long long)rows0 * a.ldc * ES,
-                                                  clamp_bytes((long long)rows * a.ldc * ES));
+                                                  out_bytes((long long)rows * a.ldc * ES));
       const __amdgpu_buffer_rsrc_t ar = make_rsrc((char*)ab + (long long)rows0 * a.ldc2 * ES,
-                                                  clamp_bytes((long long)rows * a.ldc2 * ES));
+                                                  out_bytes((long long)rows * a.ldc2 * ES));
       auto store_gate = [&](int row, int c, const float* v) {
-        if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + n0 + c), v);
+        store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + n0 + c), v);
       };
       auto store_up = [&](int row, int c, const float* v) {
-        if (row < rows && n0 + c < a.I) store8(hr, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
+        store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
       };
       auto store_act = [&](int row, int c, const float* v) {
-        if (row < rows && n0 + c < a.I) store8(ar, (uint32_t)(row * a.ldc2 + n0 + c), v);
+        store8(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
       };
       // gate slice out; then act = silu(g) * u replaces it in LDS (each
       // elane rewrites the very words it put, so no barrier in between and
@@ -771,9 +780,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           const __amdgpu_buffer_rsrc_t hr = make_rsrc(
               (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
           const __amdgpu_buffer_rsrc_t dr = make_rsrc(
-              (char*)db + (long long)rows0 * a.ldc * ES, clamp_bytes((long long)rows * a.ldc * ES));
+              (char*)db + (long long)rows0 * a.ldc * ES, out_bytes((long long)rows * a.ldc * ES));
           // d(act) -> d(gate), d(up) of act = silu(gate) * up
-          auto bwd8 = [&](int row, int i, const float* d, const float* gv, const float* uv) {
+          auto bwd8 = [&](bool ok, int row, int i, const float* d, const float* gv,
+                          const float* uv) {
             float dg[8], du[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -781,8 +791,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
               du[e] = d[e] * gv[e] * sg;
             }
-            store8(dr, (uint32_t)(row * a.ldc + i), dg);
-            store8(dr, (uint32_t)(row * a.ldc + a.I + i), du);
+            store8(dr, ok, (uint32_t)(row * a.ldc + i), dg);
+            store8(dr, ok, (uint32_t)(row * a.ldc + a.I + i), du);
           };
           if (sizeof(T) == 2) {
             // bf16: the slice's gate/up chunks (16 per thread) are
@@ -807,12 +817,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
               const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
               const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
-              if (row < rows && i < a.I) {
-                float gv[8], uv[8];
-                unpack16(graw[it], gv, T());
-                unpack16(uraw[it], uv, T());
-                bwd8(row, i, d, gv, uv);
-              }
+              float gv[8], uv[8];
+              unpack16(graw[it], gv, T());
+              unpack16(uraw[it], uv, T());
+              bwd8(row < rows && i < a.I, row, i, d, gv, uv);
             };
             // first half requested before the staging, second half after it
             // (ahead of the first half's stores)
@@ -827,12 +835,11 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           } else {
             emit(hc, [&](int row, int c, const float* d) {
               const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
-              if (row < rows && i < a.I) {
-                float gv[8], uv[8];
-                load8(hr, (uint32_t)(row * a.ldaux + i), gv);
-                load8(hr, (uint32_t)(row * a.ldaux + a.I + i), uv);
-                bwd8(row, i, d, gv, uv);
-              }
+              const bool ok = row < rows && i < a.I;
+              float gv[8], uv[8];
+              load8(hr, ok, (uint32_t)(row * a.ldaux + i), gv);
+              load8(hr, ok, (uint32_t)(row * a.ldaux + a.I + i), uv);
+              bwd8(ok, row, i, d, gv, uv);
             });
           }
         } else {
@@ -851,21 +858,29 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
             cbytes = (long long)rows * a.ldc * OS;
             lim_m = rows;
           }
-          const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, clamp_bytes(cbytes));
-          const bool f32out = a.out_f32;
-          emit(hc, [&](int row, int c, const float* v) {
+          const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, out_bytes(cbytes));
+          // (the output type is chosen outside the loop, which then
+          // unrolls into batches of LDS reads and stores)
+          auto place = [&](int row, int c, bool& ok) {
             const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
             const int m = m0 + row;
-            if (m < lim_m && n < a.N) {
-              const uint32_t e = (uint32_t)(m * a.ldc + n);
-              if (f32out) {
-                buf_store16(cr, e * 4u, pack16(v, 0.0f));
-                buf_store16(cr, e * 4u + 16u, pack16(v + 4, 0.0f));
-              } else {
-                store8(cr, e, v);
-              }
-            }
-          });
+            ok = m < lim_m && n < a.N;
+            return (uint32_t)(m * a.ldc + n);
+          };
+          if (a.out_f32) {
+            emit(hc, [&](int row, int c, const float* v) {
+              bool ok;
+              const uint32_t e = place(row, c, ok);
+              buf_store16(cr, ok ? e * 4u : DROP, pack16(v, 0.0f));
+              buf_store16(cr, ok ? e * 4u + 16u : DROP, pack16(v + 4, 0.0f));
+            });
+          } else {
+            emit(hc, [&](int row, int c, const float* v) {
+              bool ok;
+              const uint32_t e = place(row, c, ok);
+              store8(cr, ok, e, v);
+            });
+          }
         }
       };
       slice(std::integral_constant<int, 0>{});
