@@ -107,11 +107,24 @@ def cpu_baseline(cfg_name, tokens, min_seconds=10.0, max_reps=8):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        deps = np.show_config(mode="dicts")["Build Dependencies"]
+        blas = ", ".join(f"{k}: {deps[k].get('name', '?')} {deps[k].get('version', '')}".strip()
+                         for k in ("blas", "lapack") if k in deps)
+    except Exception:
+        blas = "unknown"
     return {"value": tokens * reps / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{cfg_name} layer fwd+bwd on {tokens} tokens (same H/I/E/k and seeds as "
                       f"the workload), numpy fp32 on bf16 inputs, {reps} repetitions, "
-                      f"{spent:.1f} s", "seconds": spent,
-            "cpu": platform.processor() or platform.machine()}
+                      f"{spent:.1f} s", "seconds": spent, "cpu": cpu_model, "blas": blas}
 
 
 def measured_traffic(call):
