@@ -9,7 +9,9 @@ Sources (the web pages this project follows; cited by title and section):
 * [CANN-MoE]   "MoE算子优化：动态路由硬件加速与零拷贝通信实践" (gtnt.cn):
   s2.1 routing is Softmax -> Top-k selection -> mask generation;
   s2.2 an expert is a stack of fully-connected layers;
-  s4.2 the router network is kept in FP32.
+  s4.2 the router network is kept in FP32;
+  s4.3 a load-balancing term, 0.01 times the coefficient of variation of the
+  experts' loads, is added to the loss.
 * [MoE-ops]    Huawei MoE training operator article (feedman.me): the
   VectorSort section (Fig. 3) names the reorder and anti-reorder of tokens
   around the expert matmuls; the Host-Device section (Fig. 4) removes the host
@@ -37,7 +39,10 @@ notes of the repository):
 6. dropless: every one of the T*k (token, slot) pairs gets a row;
 7. experts outside the window ``[g0, g0+G)`` are remote: their rows are moved
    by permute/combine but their expert output (and its input gradient) is zero
-   and they get no weight gradient.
+   and they get no weight gradient;
+8. an expert's load is its share of the T*k rows, cv is the population
+   standard deviation over the mean, an EP group is a run of consecutive
+   experts.
 
 Precision: every function computes in the dtype ``acc`` it is given (float64
 by default).  Router logits are rounded to fp32 because [CANN-MoE] s4.2 keeps
@@ -54,7 +59,7 @@ __all__ = [
     "router_logits", "softmax", "route", "permute", "silu", "expert_forward",
     "grouped_forward", "combine", "combine_backward", "expert_backward",
     "grouped_backward", "permute_backward", "route_backward",
-    "router_backward", "layer_forward", "layer_backward",
+    "router_backward", "layer_forward", "layer_backward", "load_stats",
 ]
 
 WeightSource = Union[np.ndarray, Callable[[int], np.ndarray]]
@@ -278,6 +283,40 @@ def router_backward(dlogits: np.ndarray, x: np.ndarray, wg: np.ndarray, acc=np.f
     """Backward of ``x Wg + b``: (dx, dWg, dbias)."""
     dl = np.asarray(dlogits, acc)
     return dl @ np.asarray(wg, acc).T, np.asarray(x, acc).T @ dl, dl.sum(axis=0)
+
+
+# --------------------------------------------------------------------------
+# routing statistics
+
+
+def load_stats(counts: np.ndarray, experts_per_group: int = 1):
+    """Per-expert load and its spread, from the permute's histogram.
+
+    [CANN-MoE] s4.3 adds a balance term ``0.01 * cv(experts_load)`` to the
+    loss; [Pangu-QA] "MoE training analysis" balances per EP group and plans
+    expert placement from the experts' observed loads.  Readings (the pages
+    define none of these): ``load[e] = counts[e] / sum(counts)``; cv is the
+    population standard deviation over the mean (divide by the number of
+    experts, not one less); EP group g holds the experts
+    ``[g*epg, (g+1)*epg)``.  Returns ``(load [E], cv_experts, group_counts
+    [E/epg], cv_groups)``; cv is 0 when every count is 0.
+    """
+    c = np.asarray(counts, np.int64)
+    E = c.shape[0]
+    if E % experts_per_group:
+        raise ValueError("experts_per_group must divide E")
+    total = int(c.sum())
+    load = c.astype(np.float64) / total if total else np.zeros(E)
+
+    def cv(v):
+        v = np.asarray(v, np.float64)
+        mean = v.mean()
+        if mean == 0:
+            return 0.0
+        return float(np.sqrt(((v - mean) ** 2).mean()) / mean)
+
+    groups = c.reshape(E // experts_per_group, experts_per_group).sum(axis=1)
+    return load, cv(c), groups, cv(groups)
 
 
 # --------------------------------------------------------------------------

@@ -361,7 +361,32 @@ def check_layer_fd(O):
         assert abs(fd - bwd["dw13"][pos]) < 1e-5 * max(1, abs(fd)), (pos, fd, bwd["dw13"][pos])
 
 
+def check_load_stats_closed_forms(O):
+    """cv closed forms: equal loads 0; one expert holding every row sqrt(E-1);
+    counts (1, 3) give 0.5 (population std 1 over mean 2, not the sample
+    std's 0.707); group sums; loads sum to 1; no rows gives zeros."""
+    load, cv, g, gcv = O.load_stats(np.full(8, 5), 2)
+    assert cv == 0.0 and gcv == 0.0 and np.allclose(load, 1 / 8) and list(g) == [10] * 4
+    for E in (2, 8, 256):
+        c = np.zeros(E, np.int64)
+        c[E // 3] = 1000
+        _, cv, _, _ = O.load_stats(c)
+        assert abs(cv - np.sqrt(E - 1)) < 1e-12 * np.sqrt(E)
+    load, cv, g, gcv = O.load_stats(np.array([1, 3]), 1)
+    assert abs(cv - 0.5) < 1e-15 and np.allclose(load, [0.25, 0.75]) and list(g) == [1, 3]
+    load, cv, g, gcv = O.load_stats(np.array([1, 3, 2, 2]), 2)
+    assert list(g) == [4, 4] and gcv == 0.0 and abs(cv - np.sqrt(0.5) / 2) < 1e-15
+    r = np.random.default_rng(5)
+    c = r.integers(0, 100, 64)
+    load, cv, g, gcv = O.load_stats(c, 8)
+    assert abs(load.sum() - 1) < 1e-12 and int(g.sum()) == int(c.sum())
+    assert abs(cv - np.std(c) / np.mean(c)) < 1e-12
+    load, cv, g, gcv = O.load_stats(np.zeros(4, np.int64), 4)
+    assert cv == 0.0 and gcv == 0.0 and not load.any() and list(g) == [0]
+
+
 ALL_CHECKS = [
+    check_load_stats_closed_forms,
     check_route_bruteforce, check_route_hand_example, check_gate_closed_forms,
     check_route_backward_fd, check_permute_invariants, check_identity_experts,
     check_expert_forward_bruteforce, check_dense_special_case, check_grouped_matches_per_group,

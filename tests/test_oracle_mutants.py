@@ -115,6 +115,30 @@ def _dropped_shared(O):
     return layer_forward
 
 
+def _sample_std_cv(O):
+    orig = O.load_stats
+
+    def load_stats(counts, experts_per_group=1):
+        load, cv, g, gcv = orig(counts, experts_per_group)
+        E, G = len(counts), len(g)
+        fix = lambda v, n: v * np.sqrt(n / (n - 1)) if n > 1 else v
+        return load, fix(cv, E), g, fix(gcv, G)
+    return load_stats
+
+
+def _strided_groups(O):
+    orig = O.load_stats
+
+    def load_stats(counts, experts_per_group=1):
+        c = np.asarray(counts, np.int64)
+        G = len(c) // experts_per_group
+        load, cv, _, _ = orig(c, experts_per_group)
+        g = c.reshape(experts_per_group, G).sum(axis=0)   # expert e in group e % G
+        _, gcv, _, _ = orig(g, 1)
+        return load, cv, g, gcv
+    return load_stats
+
+
 MUTANTS = {
     "renormalised_gates": ("route", _renormalised_gates),
     "ties_to_higher_index": ("route", _ties_to_higher_index),
@@ -125,6 +149,8 @@ MUTANTS = {
     "route_bwd_sign": ("route_backward", _route_bwd_sign),
     "silu_grad_missing_term": ("expert_backward", _silu_grad_missing_term),
     "dropped_shared": ("layer_forward", _dropped_shared),
+    "sample_std_cv": ("load_stats", _sample_std_cv),
+    "strided_groups": ("load_stats", _strided_groups),
 }
 
 
