@@ -9,7 +9,7 @@ intermediate 2048, SwiGLU) plus one always-on shared expert (intermediate
 Inputs are seeded synthetic tensors (no dataset), resident in HBM before the
 timed region.
 
-A step is the whole path: router projection, route, permute, grouped GEMM
+A step is the whole path: router projection, route, permute, load statistics, grouped GEMM
 forward (+ shared expert), unpermute/combine, combine backward, grouped GEMM
 dX and dW (+ shared expert), route backward, router backward, permute
 backward.  ``value`` is tokens per second over the timed steps.
@@ -52,7 +52,7 @@ def parse():
     return p.parse_args()
 
 
-CALLS = ["router_fwd", "route", "permute", "gmm_fwd", "combine", "combine_bwd", "gmm_bwd_dx",
+CALLS = ["router_fwd", "route", "permute", "load_stats", "gmm_fwd", "combine", "combine_bwd", "gmm_bwd_dx",
          "gmm_bwd_dw", "route_bwd", "router_bwd", "permute_bwd"]
 
 
@@ -68,6 +68,7 @@ def algorithmic(cfg, rows_local):
         "router_fwd": {"flops": 2.0 * T * H * E, "bytes": T * H * b + H * E * 4 + T * E * 4},
         "route": {"bytes": 4.0 * T * E + 8.0 * T * k},
         "permute": {"bytes": (1 + k) * T * H * b + 12.0 * T * k},
+        "load_stats": {"bytes": 8.0 * E + 8 + 4.0 * (E // (cfg.groups if E % cfg.groups == 0 else E))},
         "gmm_fwd": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 3 * I) * b},
         "combine": {"bytes": (k + 1) * T * H * b + 8.0 * T * k + (T * H * b if cfg.shared else 0)},
         "combine_bwd": {"bytes": T * H * b + 2.0 * T * k * H * b + 12.0 * T * k},

@@ -133,6 +133,23 @@ int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, 
                 void* xp, int32_t* counts, int32_t* offsets, int32_t* row_id_map,
                 int32_t* src_token, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Load statistics of one routing step, from the per-expert counts (e.g.
+ * moe_permute's), for the balance term of [CANN-MoE] s4.3 (0.01 times the
+ * coefficient of variation of the experts' loads) and for an EP planner that
+ * watches per-group loads ([Pangu-QA] MoE training analysis):
+ *   load[e]          = counts[e] / N, N = sum of counts       fp32 [E], nullable
+ *   group_counts[g]  = sum of counts[e], g*epg <= e < (g+1)*epg  int32 [E/epg], nullable
+ *   cv[0]            = std(counts) / mean(counts)              fp32
+ *   cv[1]            = std(group_counts) / mean(group_counts)  fp32 ([2], nullable)
+ * std is the population standard deviation (divided by the number of
+ * values).  When N == 0 every load and both cv are 0.  epg (experts per EP
+ * group) must divide E; epg == E gives one group (cv[1] = 0).  One block,
+ * fp64 inside, each output rounded once to its type.  counts must be >= 0
+ * with N < 2^31 (true for moe_permute's; not checked on the device).
+ */
+int moe_load_stats(const int32_t* counts, int E, int experts_per_group, float* load, float* cv,
+                   int32_t* group_counts, moe_stream_t stream);
+
 /* Backward of the permute (adjoint of the row copy), fp32 sums:
  *   dx[t,:] = sum_j dxp[row_id_map[t,j],:] + add0[t,:] + add1[t,:]
  * add0/add1 are optional [T,H] tensors of type dt (nullable), e.g. the shared

@@ -53,6 +53,7 @@ _SIGS = {
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_load_stats": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "moe_permute_bwd": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_unpermute_combine_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
@@ -149,6 +150,11 @@ def moe_permute(x, dt, idx, T, H, E, k, xp, counts, offsets, row_id_map, src_tok
                 ws_bytes, stream=None):
     _call("moe_permute", addr(x), dt, addr(idx), T, H, E, k, addr(xp), addr(counts),
           addr(offsets), addr(row_id_map), addr(src_token), addr(ws), ws_bytes, _stream(stream))
+
+
+def moe_load_stats(counts, E, experts_per_group, load, cv, group_counts, stream=None):
+    _call("moe_load_stats", addr(counts), E, experts_per_group, addr(load), addr(cv),
+          addr(group_counts), _stream(stream))
 
 
 def moe_permute_bwd(dxp, row_id_map, dt, T, H, k, add0, add1, dx, stream=None):

@@ -117,6 +117,55 @@ __global__ __launch_bounds__(1024) void permute_zero_kernel(int32_t* counts, int
   }
 }
 
+// ---------------------------------------------------------------- load statistics
+
+// Fixed-order sum over the block (shuffle tree per wave, then the 16 wave
+// sums in order): bitwise the same on every run.
+__device__ __forceinline__ double stats_block_sum(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  __syncthreads();                       // red is free again
+  if (threadIdx.x % MOE_WAVE == 0) red[threadIdx.x / MOE_WAVE] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < 1024 / MOE_WAVE; ++w) s += red[w];
+  return s;
+}
+
+// Per-expert load, cv of the loads, EP-group counts and their cv from one
+// step's counts (moe_load_stats).  One block of 1024 threads, thread i owns
+// expert i and, for i < E / epg, EP group i.  fp64 inside.
+__global__ __launch_bounds__(1024) void load_stats_kernel(const int32_t* __restrict__ counts,
+                                                          int E, int epg,
+                                                          float* __restrict__ load,
+                                                          float* __restrict__ cv,
+                                                          int32_t* __restrict__ group_counts) {
+  __shared__ int cnt[1024];
+  __shared__ double red[1024 / MOE_WAVE];
+  const int i = threadIdx.x;
+  const int c = i < E ? counts[i] : 0;
+  cnt[i] = c;
+  // counts are integers below 2^31 and at most 1024 of them: the fp64 sum is exact
+  const double total = stats_block_sum((double)c, red);
+  const double mean = total / E;
+  const double d = i < E ? (double)c - mean : 0.0;
+  const double var = stats_block_sum(d * d, red) / E;
+  if (load != nullptr && i < E) load[i] = total > 0.0 ? (float)((double)c / total) : 0.f;
+  const int G = E / epg;
+  double gs = 0.0;
+  if (i < G) {
+    for (int j = 0; j < epg; ++j) gs += (double)cnt[i * epg + j];
+    if (group_counts != nullptr) group_counts[i] = (int32_t)gs;
+  }
+  const double gmean = total / G;
+  const double gd = i < G ? gs - gmean : 0.0;
+  const double gvar = stats_block_sum(gd * gd, red) / G;
+  if (cv != nullptr && i == 0) {
+    cv[0] = total > 0.0 ? (float)(sqrt(var) / mean) : 0.f;
+    cv[1] = total > 0.0 ? (float)(sqrt(gvar) / gmean) : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------- scatter
 
 template <int ESZ>
@@ -463,6 +512,23 @@ extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int
     hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
                        offsets, hist, T, H, E, k, xp, row_id_map, src_token);
   return moe_check_launch("moe_permute(scatter)");
+}
+
+extern "C" int moe_load_stats(const int32_t* counts, int E, int experts_per_group, float* load,
+                              float* cv, int32_t* group_counts, moe_stream_t stream) {
+  const char* fn = "moe_load_stats";
+  if (E < 1 || E > MOE_MAX_E)
+    return moe_fail(MOE_ERR_UNSUPPORTED, "%s: E = %d outside [1, %d]", fn, E, MOE_MAX_E);
+  if (experts_per_group < 1 || E % experts_per_group != 0)
+    return moe_fail(MOE_ERR_INVALID_ARG, "%s: experts_per_group = %d does not divide E = %d", fn,
+                    experts_per_group, E);
+  MOE_TRY(moe_need_ptr(counts, fn, "counts", 4));
+  MOE_TRY(moe_opt_ptr(load, fn, "load", 4));
+  MOE_TRY(moe_opt_ptr(cv, fn, "cv", 4));
+  MOE_TRY(moe_opt_ptr(group_counts, fn, "group_counts", 4));
+  hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, counts, E,
+                     experts_per_group, load, cv, group_counts);
+  return moe_check_launch(fn);
 }
 
 extern "C" int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int dt, int T, int H,

@@ -83,6 +83,11 @@ class MoeLayer:
         self.counts = e(E, d=i32)
         self.offsets = e(E + 1, d=i32)
         self.row_id_map = e(T, k, d=i32)
+        # load statistics; an EP group is the window of experts one device runs
+        self.epg = s.groups if E % s.groups == 0 else E
+        self.load = e(E, d=f32)
+        self.cv = e(2, d=f32)
+        self.group_counts = e(E // self.epg, d=i32)
         self.src_token = e(R, d=i32)
         self.ws_bytes = abi.moe_permute_workspace_bytes(T, E, k)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -155,6 +160,10 @@ class MoeLayer:
         abi.moe_permute(self.x, self.dt, self.idx, s.T, s.H, s.E, s.k, self.xp, self.counts,
                         self.offsets, self.row_id_map, self.src_token, self.ws, self.ws_bytes,
                         stream)
+
+    def load_stats(self, stream=None):
+        abi.moe_load_stats(self.counts, self.s.E, self.epg, self.load, self.cv, self.group_counts,
+                           stream)
 
     def _gmm_sel(self, part):
         """(G, shared descriptor, workspace) of one grouped-GEMM launch set:
@@ -232,6 +241,7 @@ class MoeLayer:
                 self.router_fwd(main)
             self.route(main)
             self.permute(main)
+            self.load_stats(main)
             self.gmm_fwd(main, part="routed")
             main.wait_event(ev_sh)
             self.combine(main)
@@ -240,6 +250,7 @@ class MoeLayer:
             self.router_fwd(stream)
         self.route(stream)
         self.permute(stream)
+        self.load_stats(stream)
         self.gmm_fwd(stream)
         self.combine(stream)
 

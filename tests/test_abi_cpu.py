@@ -116,6 +116,21 @@ def test_shape_limits(abi):
     assert st == abi.MOE_ERR_UNSUPPORTED
 
 
+def test_load_stats_rejects_bad_arguments(abi):
+    st = status(abi, "moe_load_stats", FAKE, 0, 1, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    st = status(abi, "moe_load_stats", FAKE, 2048, 1, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
+    st = status(abi, "moe_load_stats", FAKE, 64, 6, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG and "does not divide" in abi.moe_last_error()
+    st = status(abi, "moe_load_stats", FAKE, 64, 0, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG
+    st = status(abi, "moe_load_stats", None, 64, 8, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG and "counts is NULL" in abi.moe_last_error()
+    st = status(abi, "moe_load_stats", FAKE, 64, 8, FAKE_ODD, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_INVALID_ARG
+
+
 def test_binding_raises_with_detail(abi):
     with pytest.raises(abi.MoeError) as ei:
         abi.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, stream=0)

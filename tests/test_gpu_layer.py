@@ -65,6 +65,10 @@ def check_layer(name, dynamic=True, overlap=True, **overrides):
     assert rel_err(host(L.gate), fwd["gate"]) <= 1e-5
     assert np.array_equal(host(L.counts), fwd["counts"])
     assert np.array_equal(host(L.offsets), fwd["offsets"])
+    load, cv, gc, gcv = oracle.load_stats(fwd["counts"], L.epg)
+    assert np.array_equal(host(L.group_counts), gc)
+    assert np.allclose(host(L.load), load, rtol=2.0 ** -23, atol=0)
+    assert np.allclose(host(L.cv), [cv, gcv], rtol=2.0 ** -23, atol=0)
     assert np.array_equal(host(L.row_id_map), fwd["row_id_map"])
     assert np.array_equal(host(L.src_token), fwd["src_token"])
     assert np.array_equal(host(L.xp), fwd["xp"])
