@@ -127,6 +127,9 @@ int moe_route_bwd(const float* logits, const int32_t* idx, const float* dgate,
  *   src_token[r]    token that row r came from                           [T*k]
  *   xp[r,:]         = x[src_token[r],:], a bit copy                      [T*k,H]
  * ws must hold moe_permute_workspace_bytes(T,E,k) bytes (contents scratch).
+ * xp may be NULL: then only counts, offsets and the maps are written (no row
+ * is copied, x may be NULL too) -- the recompute variant below reads token
+ * rows from x through src_token instead.
  */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
@@ -216,7 +219,9 @@ typedef struct moe_shared_expert {
 /* Forward:  h13 = xp . w13[e]^T        (saved, [R,2I])
  *           act = silu(h13[:, :I]) * h13[:, I:]   (saved, [R,I]; silu(z) = z/(1+e^-z))
  *           yp  = act . w2[e]^T        ([R,H])
- * The activation is applied to the fp32 accumulators before rounding. */
+ * The activation is computed in fp32 from the gate and up values as h13
+ * stores them (rounded to dt), so the backward, which reads h13, and
+ * moe_grouped_gemm_bwd_dw_recompute see the same g and u. */
 int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
                          int dt, int H, int I, const void* w13, const void* w2,
                          void* h13, void* act, void* yp, const moe_shared_expert* shared,
@@ -241,6 +246,41 @@ int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp, co
                             const int32_t* offsets, int g0, int G, int R, int dt, int H, int I,
                             void* dw13, void* dw2, const moe_shared_expert* shared,
                             void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------- recompute variant
+ * Fine-grained recompute in place of saved activations ([Pangu-QA], the
+ * memory-saving part: modules such as the permute and the activation
+ * function are recomputed instead of the whole layer): neither xp nor act has
+ * to live from the forward to the backward.
+ *  - moe_permute with xp == NULL builds the maps only;
+ *  - moe_grouped_gemm_fwd_gather reads routed row r of the first product from
+ *    x[src_token[r]] (x [T,H], src_token [R] from moe_permute); the rest is
+ *    moe_grouped_gemm_fwd (act [R,I] is still written: the second product
+ *    reads it, but nothing needs it afterwards);
+ *  - moe_grouped_gemm_bwd_dw_recompute first recomputes act from h13 for the
+ *    routed window (rows [offsets[g0], offsets[g0+G])) and for the shared
+ *    expert (shared->act from shared->h13), writing it to act / shared->act
+ *    (scratch of the call), then computes moe_grouped_gemm_bwd_dw with the
+ *    routed xp rows read as x[src_token[r]].  The shared expert reads
+ *    shared->x as before.
+ * moe_grouped_gemm_bwd_dx needs neither xp nor act and is shared by both
+ * variants.  Results are bitwise equal to the saving variant's (the same
+ * products in the same order; act is recomputed from the same rounded h13).
+ * bf16 only (MOE_ERR_UNSUPPORTED for MOE_F32); x must be below 2 GiB.
+ * src_token entries outside [0, T) read zero rows (never out of bounds).
+ */
+int moe_grouped_gemm_fwd_gather(const void* x, const int32_t* src_token, int T,
+                                const int32_t* offsets, int g0, int G, int R, int dt, int H,
+                                int I, const void* w13, const void* w2, void* h13, void* act,
+                                void* yp, const moe_shared_expert* shared, void* ws,
+                                size_t ws_bytes, moe_stream_t stream);
+
+int moe_grouped_gemm_bwd_dw_recompute(const void* x, const int32_t* src_token, int T,
+                                      const void* h13, void* act, const void* dyp,
+                                      const void* dh13, const int32_t* offsets, int g0, int G,
+                                      int R, int dt, int H, int I, void* dw13, void* dw2,
+                                      const moe_shared_expert* shared, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream);
 
 #ifdef __cplusplus
 }

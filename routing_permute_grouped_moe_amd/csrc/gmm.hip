@@ -79,6 +79,10 @@ struct GmmArgs {
   // tile scheduler counters (NULL: static tile order): 8 per-XCD tile
   // counters and a finished-workgroup counter, zero on entry and on exit
   int* cnt;
+  // row gather (kernels built with GATHER): routed row r of the token
+  // operand is row gather[r] of X (gather_rows rows) instead of row r --
+  // FWD1's A rows, DW's Q rows (the K rows of the second factor)
+  const int32_t* gather; int gather_rows;
 };
 
 // Per element type: K step BK (KS MFMA k-steps), ring of STAGES stages of two
@@ -229,6 +233,40 @@ __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
   }
 }
 
+// K-major, rows gathered: tile row `row` (< rows) is row gather[rows0 + row]
+// of the view; the indices are read once per tile.
+template <typename T>
+__device__ __forceinline__ void kmajor_offsets_gather(const View& v, const int32_t* gather,
+                                                      int rows0, int rows,
+                                                      uint32_t (&off)[Cfg<T>::DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
+  constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t gi = make_rsrc(gather + rows0, (uint32_t)rows * 4u);
+  int src[DPO];
+#pragma unroll
+  for (int j = 0; j < DPO; ++j) {
+    const int row = (wave * DPO + j) * RPC + lane / LPR;
+    src[j] = (int)buf_load4(gi, (uint32_t)row * 4u);    // row >= rows reads 0, masked below
+  }
+#pragma unroll
+  for (int j = 0; j < DPO; ++j) {
+    const int row = (wave * DPO + j) * RPC + lane / LPR;
+    const int chunk = (lane % LPR) ^ kswz<T>(row);
+    off[j] = row < rows ? (uint32_t)src[j] * (uint32_t)(v.ld * ES) + (uint32_t)(chunk * VEC * ES)
+                        : OOB;
+  }
+}
+
+// One 256-byte HBM -> LDS copy of 4-byte words: lane l's word at voff + soff
+// lands at lds + 4 l (the row indices of a gathered operand).
+__device__ __forceinline__ void dma4(const i32x4& rs, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(uniform(soff)), "{m0}"(uniform((int)lds))
+               : "memory");
+}
+
 template <int DPO>
 __device__ __forceinline__ void issue_op(const View& v, const char* lds_op,
                                          const uint32_t (&off)[DPO], int soff) {
@@ -306,10 +344,29 @@ __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// act = silu(g) * u from the gate and up values as h13 stores them (rounded
+// to T), so the backward's derivative and a recomputed act see the very
+// same g and u as the forward
+template <typename T>
+__device__ __forceinline__ float swiglu_act(float g, float u) {
+  if constexpr (sizeof(T) == 2) {
+    g = bf16_to_f32(f32_to_bf16(g));
+    u = bf16_to_f32(f32_to_bf16(u));
+  }
+  return g * sigmoidf_(g) * u;
+}
+
 // ---------------------------------------------------------------- the kernel
-template <typename T, int MODE>
+template <typename T, int MODE, bool GATHER = false>
 __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
+  // DW with gathered Q rows: the rows change every K step, so each wave also
+  // copies its K rows' indices into an LDS ring, two steps before the copies
+  // that use them -- one more buffer load per wave per step (GI)
+  constexpr bool GLOOP = GATHER && MODE == DW;
+  constexpr int GI = GLOOP ? 1 : 0;
+  static_assert(!GATHER || MODE == FWD1 || MODE == DW, "rows are gathered in FWD1 and DW");
+  static_assert(!GLOOP || sizeof(T) == 2, "gathered DW is built for bf16");
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
   constexpr int STAGES = Cfg<T>::STAGES, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
@@ -322,6 +379,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
   __shared__ int g_kp[MOE_MAX_E + 2];   // DW: K steps before each group in work order
   __shared__ int s_next;
+  // GLOOP: [wave][step % 4][64] row indices (lanes 0-7 of each copy carry them)
+  __shared__ __attribute__((aligned(16))) int g_idx[GLOOP ? (NT / 64) * 4 * 64 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -488,6 +547,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
     rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
     const bool sh = g >= a.G;
+    const bool gat = GATHER && !sh;   // routed tile of a gathering launch
     const long long xg = a.dense ? (long long)g * a.x_gs * ES : 0;   // dense group bases
     const int arows = a.kwrap > 0 ? a.kwrap : kdim;   // A rows a DW tile can touch
 
@@ -495,8 +555,11 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     View va, vb;
     if constexpr (MODE != DW) {
       const void* xb = sh ? a.sX : (const void*)((const char*)a.X + xg);
-      va = make_view((const char*)xb + (long long)rows0 * a.ldx * ES, (long long)rows * a.ldx * ES,
-                     a.ldx, rows);
+      if (gat)   // FWD1: the rows are gathered from the whole token matrix
+        va = make_view(a.X, (long long)a.gather_rows * a.ldx * ES, a.ldx, rows);
+      else
+        va = make_view((const char*)xb + (long long)rows0 * a.ldx * ES,
+                       (long long)rows * a.ldx * ES, a.ldx, rows);
       const void* wb = sh ? a.sW : (const void*)((const char*)a.W + (long long)g * a.w_gs * ES);
       const int wrows = (MODE == FWD1) ? 2 * a.I : (B_MN ? a.K : a.N);  // stored rows of W
       const int wcols = B_MN ? a.N : a.K;
@@ -506,8 +569,11 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       const void* qb = sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)g * a.w_gs * ES : 0));
       va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
                      a.ldx, a.M);
-      vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES, (long long)kdim * a.ldw * ES,
-                     a.ldw, a.N);
+      if (gat)   // DW: Q's K rows are gathered from the whole token matrix
+        vb = make_view(a.W, (long long)a.gather_rows * a.ldw * ES, a.ldw, a.N);
+      else
+        vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES,
+                       (long long)kdim * a.ldw * ES, a.ldw, a.N);
     }
 
     f32x16 acc[FM][FN];
@@ -521,11 +587,19 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const int KT = (kdim + BK - 1) / BK;   // K steps with data
     uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
     if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
+    else if (GATHER && MODE == FWD1 && gat)
+      kmajor_offsets_gather<T>(va, a.gather, rows0, rows, offa);
     else kmajor_offsets<T, false>(va, m0, 0, offa);
-    if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
+    if constexpr (GLOOP) {
+      // gathered Q: only the column part is fixed; the row part comes with
+      // each K step's indices (view with ld 0 gives column offsets)
+      View vc = vb;
+      if (gat) vc.ld = 0;
+      mnmajor_offsets<T>(vc, n0, offb);
+    } else if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
     else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
     const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
-    const int sb = B_MN ? vb.ld * BK * ES : BK * ES;
+    const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
     const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
     auto issue = [&](int kt) {
       const char* st = smem + (kt % STAGES) * STAGE_BYTES;
@@ -551,16 +625,64 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
     };
     auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
+    // GLOOP: B copy j of a step covers K rows 8 wave + 2 j + (0, 1), lane l
+    // the row l / 32.  The indices of a wave's 8 rows of step kt are copied
+    // to its slot kt % 4 in the order 0 2 4 6 1 3 5 7, so a lane's four
+    // indices are one 16-byte read.
+    const int hrow = lane >> 5;
+    i32x4 rs_g = rs_none;
+    uint32_t goff = OOB;
+    if constexpr (GLOOP) {
+      if (gat)
+        rs_g = raw_rsrc((const char*)a.gather + (long long)rows0 * 4,
+                        clamp_bytes((long long)kdim * 4));
+      goff = lane < 8 ? (uint32_t)((8 * wave + 2 * (lane & 3) + (lane >> 2)) * 4) : OOB;
+    }
+    const uint32_t lds_g = lds_addr((const char*)g_idx) + (uint32_t)(wave * 4 * 256);
+    const uint32_t rowb = (uint32_t)(vb.ld * ES);
+    auto issue_idx = [&](int kt) {
+      dma4(kt < KT ? rs_g : rs_none, lds_g + (uint32_t)((kt & 3) * 256), goff, kt * BK * 4);
+    };
+    auto read_idx = [&](int kt) {
+      return *(const u32x4*)(g_idx + (wave * 4 + (kt & 3)) * 64 + 4 * hrow);
+    };
+    auto issue_b = [&](int kt, int j, const u32x4& iv) {
+      const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+      const int krow = kt * BK + 8 * wave + 2 * j + hrow;
+      const uint32_t vo =
+          gat ? ((krow < kdim && offb[j] != OOB) ? iv[j] * rowb + offb[j] : OOB) : offb[j];
+      dma16(kt < KT ? vb.rs : rs_none, st + OPB + j * 1024, vo, kt * sb);
+      if (j == DMA_PER_OP - 1 && ++ka_next == wrap_steps) ka_next = 0;
+    };
 
     if (KT > 0) {
       if constexpr (sizeof(T) == 2) {
         // steps 0, 1 and 2 in flight (empty copies past the end), so the
         // wait counts below hold for every K step
+        if constexpr (GLOOP) {
+          // indices of steps 0-2 first; then per step A, B and the indices
+          // of two steps on, in the order the loop keeps
+          issue_idx(0);
+          issue_idx(1);
+          issue_idx(2);
+          wait_vm<0>();
+          asm volatile("" ::: "memory");
+          const u32x4 iv[3] = {read_idx(0), read_idx(1), read_idx(2)};
 #pragma unroll
-        for (int kt = 0; kt < STAGES - 1; ++kt)
+          for (int kt = 0; kt < STAGES - 1; ++kt) {
 #pragma unroll
-          for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
-        wait_vm<2 * DMA_PER_STEP>();
+            for (int j = 0; j < DMA_PER_OP; ++j) issue1(kt, j);
+#pragma unroll
+            for (int j = 0; j < DMA_PER_OP; ++j) issue_b(kt, j, iv[kt]);
+            if (kt >= 1) issue_idx(kt + 2);
+          }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < STAGES - 1; ++kt)
+#pragma unroll
+            for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
+        }
+        wait_vm<2 * DMA_PER_STEP + 2 * GI>();
       } else {
         for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
         if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
@@ -600,8 +722,12 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           // (step kt+2, and step kt+3's A copies) are outstanding; the
           // barrier extends that to all waves and retires every read of the
           // stage refilled next
-          wait_vm<DMA_PER_STEP + DMA_PER_OP>();
+          // (GLOOP: also step kt+3's indices, issued right after step
+          // kt+1's B copies, and one index copy more per step since)
+          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
           __syncthreads();
+          u32x4 ivn;
+          if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -610,8 +736,12 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
               if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-              else if (q - (FM + FN) < DMA_PER_OP)
-                issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+              else if (q - (FM + FN) < DMA_PER_OP) {
+                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
+                else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+              } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
+                issue_idx(kt + STAGES + 1);
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -759,10 +889,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
               f32x4 v = *pp;
               const f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
                                acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
-              v.x = v.x * sigmoidf_(v.x) * u.x;
-              v.y = v.y * sigmoidf_(v.y) * u.y;
-              v.z = v.z * sigmoidf_(v.z) * u.z;
-              v.w = v.w * sigmoidf_(v.w) * u.w;
+              v.x = swiglu_act<T>(v.x, u.x);
+              v.y = swiglu_act<T>(v.y, u.y);
+              v.z = swiglu_act<T>(v.z, u.z);
+              v.w = swiglu_act<T>(v.w, u.w);
               *pp = v;
             }
         __syncthreads();
@@ -897,6 +1027,38 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- act recompute
+// act[r, :] = swiglu_act(h13[r, :I], h13[r, I:]) for the rows [lo, hi):
+// the routed window [offsets[g0], offsets[g0+G]) (clamped to R), or [0, n)
+// without offsets.  One 16-byte chunk of act per thread and pass.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_act_kernel(const T* __restrict__ h13,
+                                                         T* __restrict__ act,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int g0, int G, int n, int I) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
+  int lo = 0, hi = n;
+  if (offsets != nullptr) {
+    lo = min(max(offsets[g0], 0), n);
+    hi = min(max(offsets[g0 + G], lo), n);
+  }
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(h13, clamp_bytes((long long)n * 2 * I * ES));
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(act, out_bytes((long long)n * I * ES));
+  const int cpr = I / VEC;   // chunks per act row
+  const long long total = (long long)(hi - lo) * cpr;
+  for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < total;
+       c += (long long)gridDim.x * 256) {
+    const int row = lo + (int)(c / cpr), q = (int)(c % cpr);
+    const uint32_t ge = (uint32_t)row * (uint32_t)(2 * I) + (uint32_t)(q * VEC);
+    float g[VEC], u[VEC], v[VEC];
+    unpack16(buf_load16(hr, ge * ES), g, T());
+    unpack16(buf_load16(hr, (ge + (uint32_t)I) * ES), u, T());
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = swiglu_act<T>(g[e], u[e]);
+    buf_store16(ar, ((uint32_t)row * (uint32_t)I + (uint32_t)(q * VEC)) * ES, pack16(v, T()));
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 int grid_size() {
@@ -904,15 +1066,29 @@ int grid_size() {
   return n >= 8 ? (n / 8) * 8 : n;
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool GATHER = false>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
-  hipLaunchKernelGGL((gmm_kernel<T, MODE>), dim3(grid_size()), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER>), dim3(grid_size()), dim3(NT), 0, s, a);
   return moe_check_launch(what);
 }
 
 template <int MODE>
 int launch_dt(int dt, const GmmArgs& a, hipStream_t s, const char* what) {
+  if constexpr (MODE == FWD1 || MODE == DW)
+    if (a.gather != nullptr) return launch<bf16_t, MODE, true>(a, s, what);   // bf16 only
   return dt == MOE_BF16 ? launch<bf16_t, MODE>(a, s, what) : launch<float, MODE>(a, s, what);
+}
+
+// Checks of a row gather from the token matrix x [T, H] (recompute variant).
+int gather_checks(const char* fn, int dt, const void* x, const int32_t* src_token, int T, int H) {
+  if (dt != MOE_BF16)
+    return moe_fail(MOE_ERR_UNSUPPORTED, "%s: the row gather is built for bf16 only", fn);
+  MOE_TRY(moe_need_nonneg(T, fn, "T"));
+  MOE_TRY(moe_need_ptr(x, fn, "x"));
+  MOE_TRY(moe_need_ptr(src_token, fn, "src_token", 4));
+  if ((long long)T * H * 2 >= 0x80000000LL)
+    return moe_fail(MOE_ERR_UNSUPPORTED, "%s: x of %d x %d bf16 is 2 GiB or more", fn, T, H);
+  return MOE_OK;
 }
 
 int gmm_checks(const char* fn, const int32_t* offsets, int g0, int G, int R, int dt, int H, int I,
@@ -967,15 +1143,16 @@ GmmArgs base_args(const int32_t* offsets, int g0, int G, int R, const moe_shared
 
 extern "C" size_t moe_gmm_workspace_bytes(void) { return WS_BYTES; }
 
-extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
-                                    int dt, int H, int I, const void* w13, const void* w2,
-                                    void* h13, void* act, void* yp,
-                                    const moe_shared_expert* sh, void* ws, size_t ws_bytes,
-                                    moe_stream_t stream) {
-  const char* fn = "moe_grouped_gemm_fwd";
+namespace {
+
+// Forward; gather != NULL: FWD1's routed rows are x[gather[r]] (xp is x).
+int fwd_impl(const char* fn, const void* xp, const int32_t* gather, int gather_rows,
+             const int32_t* offsets, int g0, int G, int R, int dt, int H, int I, const void* w13,
+             const void* w2, void* h13, void* act, void* yp, const moe_shared_expert* sh,
+             void* ws, size_t ws_bytes, moe_stream_t stream) {
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0 && R > 0) {
-    MOE_TRY(moe_need_ptr(xp, fn, "xp"));
+    MOE_TRY(moe_need_ptr(xp, fn, gather ? "x" : "xp"));
     MOE_TRY(moe_need_ptr(w13, fn, "w13"));
     MOE_TRY(moe_need_ptr(w2, fn, "w2"));
     MOE_TRY(moe_need_ptr(h13, fn, "h13"));
@@ -998,12 +1175,14 @@ extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int 
   // FWD1: h13 = X . W13^T (N = 2I as I gate/up pairs, K = H)
   a.N = 2 * I; a.K = H; a.I = I;
   a.X = xp; a.ldx = H;
+  a.gather = gather; a.gather_rows = gather_rows;
   a.W = w13; a.ldw = H; a.w_gs = 2LL * I * H;
   a.C = h13; a.ldc = 2 * I;
   a.C2 = act; a.ldc2 = I;
   if (use_sh) { a.sX = sh->x; a.sW = sh->w13; a.sC = sh->h13; a.sC2 = sh->act; }
   MOE_TRY(launch_dt<FWD1>(dt, a, s, fn));
   // FWD2: yp = act . W2^T (N = H, K = I)
+  a.gather = nullptr;
   a.N = H; a.K = I;
   a.X = act; a.ldx = I;
   a.W = w2; a.ldw = I; a.w_gs = (long long)H * I;
@@ -1011,6 +1190,29 @@ extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int 
   a.C2 = nullptr;
   if (use_sh) { a.sX = sh->act; a.sW = sh->w2; a.sC = sh->y; a.sC2 = nullptr; }
   return launch_dt<FWD2>(dt, a, s, fn);
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
+                                    int dt, int H, int I, const void* w13, const void* w2,
+                                    void* h13, void* act, void* yp,
+                                    const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                    moe_stream_t stream) {
+  return fwd_impl("moe_grouped_gemm_fwd", xp, nullptr, 0, offsets, g0, G, R, dt, H, I, w13, w2,
+                  h13, act, yp, sh, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_grouped_gemm_fwd_gather(const void* x, const int32_t* src_token, int T,
+                                           const int32_t* offsets, int g0, int G, int R, int dt,
+                                           int H, int I, const void* w13, const void* w2,
+                                           void* h13, void* act, void* yp,
+                                           const moe_shared_expert* sh, void* ws,
+                                           size_t ws_bytes, moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_fwd_gather";
+  MOE_TRY(gather_checks(fn, dt, x, src_token, T, H));
+  return fwd_impl(fn, x, src_token, T, offsets, g0, G, R, dt, H, I, w13, w2, h13, act, yp, sh,
+                  ws, ws_bytes, stream);
 }
 
 extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G,
@@ -1059,18 +1261,23 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
   return launch_dt<DX2>(dt, a, s, fn);
 }
 
-extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp,
-                                       const void* dh13, const int32_t* offsets, int g0, int G,
-                                       int R, int dt, int H, int I, void* dw13, void* dw2,
-                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
-                                       moe_stream_t stream) {
-  const char* fn = "moe_grouped_gemm_bwd_dw";
+namespace {
+
+// Weight gradients; gather != NULL: dW13's routed K rows of xp are
+// x[gather[r]] (xp is x); h13 != NULL: act (and the shared expert's act) is
+// first recomputed from h13.
+int dw_impl(const char* fn, const void* xp, const int32_t* gather, int gather_rows,
+            const void* h13, void* act, const void* dyp, const void* dh13,
+            const int32_t* offsets, int g0, int G, int R, int dt, int H, int I, void* dw13,
+            void* dw2, const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+            moe_stream_t stream) {
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0) {
     MOE_TRY(moe_need_ptr(dw13, fn, "dw13"));
     MOE_TRY(moe_need_ptr(dw2, fn, "dw2"));
     if (R > 0) {
-      MOE_TRY(moe_need_ptr(xp, fn, "xp"));
+      if (h13) MOE_TRY(moe_need_ptr(h13, fn, "h13"));
+      MOE_TRY(moe_need_ptr(xp, fn, gather ? "x" : "xp"));
       MOE_TRY(moe_need_ptr(act, fn, "act"));
       MOE_TRY(moe_need_ptr(dyp, fn, "dyp"));
       MOE_TRY(moe_need_ptr(dh13, fn, "dh13"));
@@ -1085,10 +1292,25 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
       MOE_TRY(moe_need_ptr(sh->act, fn, "shared.act"));
       MOE_TRY(moe_need_ptr(sh->dy, fn, "shared.dy"));
       MOE_TRY(moe_need_ptr(sh->dh13, fn, "shared.dh13"));
+      if (h13) MOE_TRY(moe_need_ptr(sh->h13, fn, "shared.h13"));
     }
   }
   if (!use_sh && G == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (h13) {
+    // act of the routed window and of the shared expert, from h13
+    const int grid = 4 * grid_size();
+    if (G > 0 && R > 0) {
+      hipLaunchKernelGGL(swiglu_act_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                         (const bf16_t*)h13, (bf16_t*)act, offsets, g0, G, R, I);
+      MOE_TRY(moe_check_launch(fn));
+    }
+    if (use_sh && sh->T > 0) {
+      hipLaunchKernelGGL(swiglu_act_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                         (const bf16_t*)sh->h13, (bf16_t*)sh->act, nullptr, 0, 0, sh->T, I);
+      MOE_TRY(moe_check_launch(fn));
+    }
+  }
   GmmArgs a = base_args(offsets, g0, G, R, sh);
   MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
   a.shared = use_sh ? 1 : 0;   // an empty shared expert still gets zero gradients
@@ -1104,9 +1326,35 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
   a.M = 2 * I; a.N = H;
   a.X = dh13; a.ldx = 2 * I;
   a.W = xp; a.ldw = H;
+  a.gather = gather; a.gather_rows = gather_rows;
   a.C = dw13; a.ldc = H; a.c_gs = 2LL * I * H;
   if (use_sh) { a.sX = sh->dh13; a.sW = sh->x; a.sC = sh->dw13; }
   return launch_dt<DW>(dt, a, s, fn);
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp,
+                                       const void* dh13, const int32_t* offsets, int g0, int G,
+                                       int R, int dt, int H, int I, void* dw13, void* dw2,
+                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                       moe_stream_t stream) {
+  return dw_impl("moe_grouped_gemm_bwd_dw", xp, nullptr, 0, nullptr, const_cast<void*>(act), dyp,
+                 dh13, offsets, g0, G, R, dt, H, I, dw13, dw2, sh, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_grouped_gemm_bwd_dw_recompute(const void* x, const int32_t* src_token, int T,
+                                                 const void* h13, void* act, const void* dyp,
+                                                 const void* dh13, const int32_t* offsets,
+                                                 int g0, int G, int R, int dt, int H, int I,
+                                                 void* dw13, void* dw2,
+                                                 const moe_shared_expert* sh, void* ws,
+                                                 size_t ws_bytes, moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_bwd_dw_recompute";
+  MOE_TRY(gather_checks(fn, dt, x, src_token, T, H));
+  if (h13 == nullptr) return moe_fail(MOE_ERR_INVALID_ARG, "%s: h13 is NULL", fn);
+  return dw_impl(fn, x, src_token, T, h13, act, dyp, dh13, offsets, g0, G, R, dt, H, I, dw13,
+                 dw2, sh, ws, ws_bytes, stream);
 }
 
 

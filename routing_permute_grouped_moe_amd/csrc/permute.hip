@@ -211,6 +211,24 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
   }
 }
 
+// Row map and source tokens only (no row copy): one thread per (t, j).
+__global__ __launch_bounds__(256) void permute_maps_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ hist, int T, int E, int k, int32_t* __restrict__ row_id_map,
+    int32_t* __restrict__ src_token) {
+  const long long R = (long long)T * k;
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= R) return;
+  const int t = (int)(p / k);
+  const int c = t / PERM_CHUNK;
+  int e = idx[p];
+  e = (e >= 0 && e < E) ? e : 0;
+  long long row = (long long)offsets[e] + hist[(long long)c * E + e] + row_id_map[p];
+  row = row < 0 ? 0 : (row >= R ? R - 1 : row);
+  row_id_map[p] = (int)row;
+  src_token[row] = t;
+}
+
 // ---------------------------------------------------------------- gathers
 // The gathers below keep ROW_JB rows x ROW_QB chunks of loads in flight per
 // thread (requested together, then added in row order), so a token's k row
@@ -486,9 +504,9 @@ extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int
     hipLaunchKernelGGL(permute_zero_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E);
     return moe_check_launch("moe_permute(empty)");
   }
-  MOE_TRY(moe_need_ptr(x, fn, "x"));
+  MOE_TRY(xp ? moe_need_ptr(x, fn, "x") : moe_opt_ptr(x, fn, "x"));
   MOE_TRY(moe_need_ptr(idx, fn, "idx", 4));
-  MOE_TRY(moe_need_ptr(xp, fn, "xp"));
+  MOE_TRY(moe_opt_ptr(xp, fn, "xp"));
   MOE_TRY(moe_need_ptr(row_id_map, fn, "row_id_map", 4));
   MOE_TRY(moe_need_ptr(src_token, fn, "src_token", 4));
   MOE_TRY(moe_need_ptr(ws, fn, "ws", 4));
@@ -505,6 +523,12 @@ extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int
   MOE_TRY(moe_check_launch("moe_permute(scan)"));
   hipLaunchKernelGGL(permute_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E, offsets);
   MOE_TRY(moe_check_launch("moe_permute(offsets)"));
+  if (xp == nullptr) {
+    const long long R = (long long)T * k;
+    hipLaunchKernelGGL(permute_maps_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                       idx, offsets, hist, T, E, k, row_id_map, src_token);
+    return moe_check_launch("moe_permute(maps)");
+  }
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(permute_scatter_kernel<2>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
                        offsets, hist, T, H, E, k, xp, row_id_map, src_token);

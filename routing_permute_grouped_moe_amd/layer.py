@@ -57,9 +57,13 @@ class LayerShape:
 class MoeLayer:
     """Device buffers of one layer plus the forward/backward call sequences."""
 
-    def __init__(self, shape: LayerShape, device="cuda", overlap: bool = True):
+    def __init__(self, shape: LayerShape, device="cuda", overlap: bool = True,
+                 recompute: bool = False):
         s = self.s = shape
         self.overlap = overlap
+        # recompute: no permuted copy of x (the grouped GEMMs gather token
+        # rows through src_token) and act is recomputed from h13 for dW
+        self.recompute = recompute
         dev = self.device = torch.device(device)
         dt, f32, i32 = s.dtype, torch.float32, torch.int32
         self.dt = abi.MOE_BF16 if dt == torch.bfloat16 else abi.MOE_F32
@@ -79,7 +83,7 @@ class MoeLayer:
         # forward state
         self.idx = e(T, k, d=i32)
         self.gate = e(T, k, d=f32)
-        self.xp = e(R, H)
+        self.xp = None if recompute else e(R, H)
         self.counts = e(E, d=i32)
         self.offsets = e(E + 1, d=i32)
         self.row_id_map = e(T, k, d=i32)
@@ -165,6 +169,16 @@ class MoeLayer:
         abi.moe_load_stats(self.counts, self.s.E, self.epg, self.load, self.cv, self.group_counts,
                            stream)
 
+    def saved_bytes(self) -> int:
+        """Bytes of activations kept from the forward for the backward (beyond
+        the layer input, the weights and the routing maps)."""
+        b = self.x.element_size()
+        s = self.s
+        n = s.R * 2 * s.I + (s.T * 2 * s.I if s.shared else 0)        # h13
+        if not self.recompute:
+            n += s.R * s.H + s.R * s.I + (s.T * s.I if s.shared else 0)  # xp, act
+        return n * b
+
     def _gmm_sel(self, part):
         """(G, shared descriptor, workspace) of one grouped-GEMM launch set:
         part = "all" (routed + shared), "routed" or "shared"."""
@@ -178,6 +192,11 @@ class MoeLayer:
     def gmm_fwd(self, stream=None, part="all"):
         s = self.s
         G, sh, ws = self._gmm_sel(part)
+        if self.recompute:
+            abi.moe_grouped_gemm_fwd_gather(self.x, self.src_token, s.T, self.offsets, s.g0, G,
+                                            s.R, self.dt, s.H, s.I, self.w13, self.w2, self.h13,
+                                            self.act, self.yp, sh, ws, self.gws_bytes, stream)
+            return
         abi.moe_grouped_gemm_fwd(self.xp, self.offsets, s.g0, G, s.R, self.dt, s.H, s.I,
                                  self.w13, self.w2, self.h13, self.act, self.yp, sh, ws,
                                  self.gws_bytes, stream)
@@ -203,6 +222,12 @@ class MoeLayer:
     def gmm_bwd_dw(self, stream=None, part="all"):
         s = self.s
         G, sh, ws = self._gmm_sel(part)
+        if self.recompute:
+            abi.moe_grouped_gemm_bwd_dw_recompute(self.x, self.src_token, s.T, self.h13, self.act,
+                                                  self.dyp, self.dh13, self.offsets, s.g0, G,
+                                                  s.R, self.dt, s.H, s.I, self.dw13, self.dw2,
+                                                  sh, ws, self.gws_bytes, stream)
+            return
         abi.moe_grouped_gemm_bwd_dw(self.xp, self.act, self.dyp, self.dh13, self.offsets, s.g0,
                                     G, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh, ws,
                                     self.gws_bytes, stream)

@@ -45,9 +45,10 @@ def shape_of(cfg: synth.MoeConfig):
                       g0=cfg.g0, G=cfg.G, shared=cfg.shared, router=cfg.router)
 
 
-def make_layer(cfg: synth.MoeConfig, inp: synth.Inputs, overlap: bool = True):
+def make_layer(cfg: synth.MoeConfig, inp: synth.Inputs, overlap: bool = True,
+               recompute: bool = False):
     from routing_permute_grouped_moe_amd.layer import MoeLayer
-    L = MoeLayer(shape_of(cfg), overlap=overlap)
+    L = MoeLayer(shape_of(cfg), overlap=overlap, recompute=recompute)
     dt = torch_dtype(cfg)
     L.x.copy_(dev(inp.x, dt))
     L.dy.copy_(dev(inp.dy, dt))

@@ -131,6 +131,26 @@ def test_load_stats_rejects_bad_arguments(abi):
     assert st == abi.MOE_ERR_INVALID_ARG
 
 
+def test_recompute_variant_rejects_bad_arguments(abi):
+    # fwd_gather(x, src_token, T, offsets, g0, G, R, dt, H, I, w13, w2, h13, act, yp, sh, ws, wsb, s)
+    args = [FAKE, FAKE, 100, FAKE, 0, 4, 600, 1, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+            None, 0, None]
+    bad = list(args); bad[7] = 0                                  # fp32 storage
+    assert status(abi, "moe_grouped_gemm_fwd_gather", *bad) == abi.MOE_ERR_UNSUPPORTED
+    bad = list(args); bad[1] = None                               # no src_token
+    assert status(abi, "moe_grouped_gemm_fwd_gather", *bad) == abi.MOE_ERR_INVALID_ARG
+    bad = list(args); bad[2] = 1 << 20                            # x of 2^20 x 1024 bf16 = 2 GiB
+    bad[8] = 1024
+    assert status(abi, "moe_grouped_gemm_fwd_gather", *bad) == abi.MOE_ERR_UNSUPPORTED
+    # bwd_dw_recompute(x, src, T, h13, act, dyp, dh13, offsets, g0, G, R, dt, H, I, dw13, dw2, ...)
+    args = [FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 600, 1, 256, 128, FAKE, FAKE,
+            None, None, 0, None]
+    bad = list(args); bad[3] = None                               # no h13 to recompute from
+    assert status(abi, "moe_grouped_gemm_bwd_dw_recompute", *bad) == abi.MOE_ERR_INVALID_ARG
+    bad = list(args); bad[11] = 0
+    assert status(abi, "moe_grouped_gemm_bwd_dw_recompute", *bad) == abi.MOE_ERR_UNSUPPORTED
+
+
 def test_binding_raises_with_detail(abi):
     with pytest.raises(abi.MoeError) as ei:
         abi.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, stream=0)
