@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="pangu")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the timing of the recompute variant")
     p.add_argument("--sequential", action="store_true",
                    help="time steps with every call on one stream (the per-call breakdown is "
                         "always measured that way)")
@@ -143,11 +145,55 @@ def measured_traffic(call):
         return None
 
 
+def recompute_variant(L, steps, warmup):
+    """Time the same step with the recompute variant (no saved xp / act) on
+    the same parameters and inputs; report the activation bytes each path
+    keeps from the forward for the backward."""
+    import torch
+
+    from routing_permute_grouped_moe_amd.layer import MoeLayer
+    B = MoeLayer(L.s, overlap=L.overlap, recompute=True)
+    for n in ("x", "dy", "w13", "w2", "wg", "logits", "ws13", "ws2"):
+        if getattr(L, n) is not None:
+            getattr(B, n).copy_(getattr(L, n))
+    B.bias = L.bias
+    for _ in range(warmup):
+        B.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        B.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the calls that differ from the saving path, one stream, HIP events
+    calls = ["permute", "gmm_fwd", "gmm_bwd_dw"]
+    B.overlap = False
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls) * steps)]
+    for s in range(steps):
+        for i, c in enumerate(calls):
+            ev[2 * (s * len(calls) + i)].record(stream)
+            getattr(B, c)()
+            ev[2 * (s * len(calls) + i) + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = {c: round(sum(ev[2 * (s * len(calls) + i)].elapsed_time(
+        ev[2 * (s * len(calls) + i) + 1]) for s in range(steps)) / steps, 4)
+        for i, c in enumerate(calls)}
+    out = {"ms_per_step": round(wall * 1e3 / steps, 4),
+           "tokens_per_s": round(L.s.T * steps / wall, 1),
+           "activation_bytes_kept": B.saved_bytes(),
+           "saving_path_activation_bytes_kept": L.saved_bytes(),
+           "ms_per_call": per_call}
+    del B
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the layer here is one device's share; see the design notes on sharding)",
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the layer "
+              f"here is one device's share; the design notes describe how it would shard)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -247,6 +293,8 @@ def main():
         "roofline": roof,
         "phases": phases,
     }
+    if not args.no_variants and cfg.dtype == "bf16":
+        out["variants"] = {"recompute": recompute_variant(L, args.steps, args.warmup)}
     del L
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
