@@ -42,7 +42,11 @@ notes of the repository):
    and they get no weight gradient;
 8. an expert's load is its share of the T*k rows, cv is the population
    standard deviation over the mean, an EP group is a run of consecutive
-   experts.
+   experts;
+9. drop-and-pad (the variant the pages compare dropless with): capacity
+   C = ceil(factor * T*k / E) rows per expert, an expert keeps its first C
+   pairs in token order, dropped pairs contribute nothing, empty rows are
+   zero.
 
 Precision: every function computes in the dtype ``acc`` it is given (float64
 by default).  Router logits are rounded to fp32 because [CANN-MoE] s4.2 keeps
@@ -60,6 +64,7 @@ __all__ = [
     "grouped_forward", "combine", "combine_backward", "expert_backward",
     "grouped_backward", "permute_backward", "route_backward",
     "router_backward", "layer_forward", "layer_backward", "load_stats",
+    "capacity", "permute_capacity",
 ]
 
 WeightSource = Union[np.ndarray, Callable[[int], np.ndarray]]
@@ -138,6 +143,40 @@ def permute(x: np.ndarray, idx: np.ndarray, E: int):
     return xp, counts, offsets, row_id_map, src_token
 
 
+def capacity(T: int, k: int, E: int, factor: float) -> int:
+    """Rows per expert of the drop-and-pad variant: ``ceil(factor * T*k / E)``
+    ([CANN-MoE] s4.3 sets a capacity factor of 1.2; the pages give no
+    formula, this is the reading in which factor 1 is the mean load)."""
+    return int(np.ceil(factor * T * k / E))
+
+
+def permute_capacity(x: np.ndarray, idx: np.ndarray, E: int, C: int):
+    """Drop-and-pad permute ([CANN-MoE] s4.3 capacity factor; [Pangu-QA] MoE
+    training analysis compares it with dropless): expert e owns rows
+    ``[e*C, (e+1)*C)``; its first C pairs in token order keep a row, the rest
+    are dropped (``row_id_map = -1``); rows nobody fills are zero
+    (``src_token = -1``).  ``counts[e]`` counts every pair routed to e,
+    dropped or not; ``offsets[e] = e*C``.
+    """
+    T, k = idx.shape
+    counts = np.zeros(E, np.int64)
+    row_id_map = np.full((T, k), -1, np.int64)
+    src_token = np.full(E * C, -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            rank = counts[e]
+            counts[e] += 1
+            if rank < C:
+                row_id_map[t, j] = e * C + rank
+                src_token[e * C + rank] = t
+    offsets = np.arange(E + 1, dtype=np.int64) * C
+    xp = np.zeros((E * C,) + x.shape[1:], x.dtype)
+    kept = src_token >= 0
+    xp[kept] = x[src_token[kept]]
+    return xp, counts, offsets, row_id_map, src_token
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
@@ -179,11 +218,14 @@ def grouped_forward(xp: np.ndarray, offsets: np.ndarray, w13: WeightSource, w2: 
 def combine(yp: np.ndarray, row_id_map: np.ndarray, gate: np.ndarray,
             y_shared: Optional[np.ndarray] = None, acc=np.float64) -> np.ndarray:
     """Anti-reorder and weighted sum: ``y[t] = ys[t] + sum_j gate[t,j] yp[row(t,j)]``
-    ([MoE-ops] VectorSort; [Pangu-QA] experimental results, shared weight 1)."""
+    ([MoE-ops] VectorSort; [Pangu-QA] experimental results, shared weight 1).
+    A dropped pair (row -1, drop-and-pad variant) adds nothing."""
     T, k = row_id_map.shape
     y = np.zeros((T, yp.shape[1]), acc) if y_shared is None else np.array(y_shared, acc)
     for j in range(k):
-        y += np.asarray(gate[:, j], acc)[:, None] * np.asarray(yp[row_id_map[:, j]], acc)
+        rows = row_id_map[:, j]
+        keep = rows >= 0
+        y[keep] += np.asarray(gate[keep, j], acc)[:, None] * np.asarray(yp[rows[keep]], acc)
     return y
 
 
@@ -193,15 +235,17 @@ def combine(yp: np.ndarray, row_id_map: np.ndarray, gate: np.ndarray,
 
 def combine_backward(dy: np.ndarray, yp: np.ndarray, row_id_map: np.ndarray,
                      gate: np.ndarray, acc=np.float64):
-    """``dyp[row(t,j)] = gate[t,j] dy[t]``, ``dgate[t,j] = <dy[t], yp[row(t,j)]>``."""
+    """``dyp[row(t,j)] = gate[t,j] dy[t]``, ``dgate[t,j] = <dy[t], yp[row(t,j)]>``;
+    a dropped pair (row -1) gets dgate 0 and no row."""
     T, k = row_id_map.shape
     dy = np.asarray(dy, acc)
     dyp = np.zeros((yp.shape[0], dy.shape[1]), acc)
     dgate = np.zeros((T, k), acc)
     for j in range(k):
         rows = row_id_map[:, j]
-        dyp[rows] = np.asarray(gate[:, j], acc)[:, None] * dy
-        dgate[:, j] = np.einsum("th,th->t", dy, np.asarray(yp[rows], acc))
+        keep = rows >= 0
+        dyp[rows[keep]] = np.asarray(gate[keep, j], acc)[:, None] * dy[keep]
+        dgate[keep, j] = np.einsum("th,th->t", dy[keep], np.asarray(yp[rows[keep]], acc))
     return dyp, dgate
 
 
@@ -257,11 +301,14 @@ def grouped_backward(xp: np.ndarray, dyp: np.ndarray, offsets: np.ndarray,
 
 
 def permute_backward(dxp: np.ndarray, row_id_map: np.ndarray, acc=np.float64) -> np.ndarray:
-    """``dx[t] = sum_j dxp[row(t,j)]`` (the adjoint of the row copy)."""
+    """``dx[t] = sum_j dxp[row(t,j)]`` (the adjoint of the row copy); dropped
+    pairs (row -1) add nothing."""
     T, k = row_id_map.shape
     dx = np.zeros((T, dxp.shape[1]), acc)
     for j in range(k):
-        dx += np.asarray(dxp[row_id_map[:, j]], acc)
+        rows = row_id_map[:, j]
+        keep = rows >= 0
+        dx[keep] += np.asarray(dxp[rows[keep]], acc)
     return dx
 
 
@@ -325,14 +372,18 @@ def load_stats(counts: np.ndarray, experts_per_group: int = 1):
 
 def layer_forward(x, k: int, E: int, w13: WeightSource, w2: WeightSource,
                   wg=None, bias=None, logits=None, g0: int = 0, G: Optional[int] = None,
-                  ws13=None, ws2=None, acc=np.float64) -> dict:
+                  ws13=None, ws2=None, acc=np.float64, C: Optional[int] = None) -> dict:
     """Route -> permute -> grouped SwiGLU -> unpermute/combine (+ shared expert).
 
-    Either ``wg`` (router weights) or ``logits`` must be given."""
+    Either ``wg`` (router weights) or ``logits`` must be given.  ``C`` (rows
+    per expert) selects the drop-and-pad variant; None is dropless."""
     if logits is None:
         logits = router_logits(x, wg, bias)
     idx, gate = route(logits, k, acc)
-    xp, counts, offsets, row_id_map, src_token = permute(x, idx, E)
+    if C is None:
+        xp, counts, offsets, row_id_map, src_token = permute(x, idx, E)
+    else:
+        xp, counts, offsets, row_id_map, src_token = permute_capacity(x, idx, E, C)
     h13, act, yp = grouped_forward(xp, offsets, w13, w2, g0, G, acc)
     ys = None
     if ws13 is not None:

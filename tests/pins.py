@@ -385,8 +385,86 @@ def check_load_stats_closed_forms(O):
     assert cv == 0.0 and gcv == 0.0 and not load.any() and list(g) == [0]
 
 
+def check_capacity_bruteforce(O):
+    """Drop-and-pad permute against a direct listing: expert e's pairs in
+    (token, slot) order, the first C keep rows e*C.., the rest are dropped;
+    pad rows are zero with source -1; kept + dropped = T*k."""
+    r = np.random.default_rng(41)
+    T, k, E, C, H = 13, 2, 4, 3, 5
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    logits[:, 1] += 1.5                                       # expert 1 overflows
+    idx, _ = O.route(logits, k)
+    x = r.standard_normal((T, H))
+    xp, counts, offsets, rmap, src = O.permute_capacity(x, idx, E, C)
+    assert list(offsets) == [0, 3, 6, 9, 12] and xp.shape == (E * C, H)
+    kept = 0
+    for e in range(E):
+        pairs = [(t, j) for t in range(T) for j in range(k) if idx[t, j] == e]
+        assert counts[e] == len(pairs)
+        for n, (t, j) in enumerate(pairs):
+            if n < C:
+                assert rmap[t, j] == e * C + n and src[e * C + n] == t
+                assert np.array_equal(xp[e * C + n], x[t])
+                kept += 1
+            else:
+                assert rmap[t, j] == -1
+        for n in range(len(pairs), C):
+            assert src[e * C + n] == -1 and not xp[e * C + n].any()
+    assert kept + int((rmap < 0).sum()) == T * k and kept == int((src >= 0).sum())
+    assert max(counts) > C                                     # something was dropped
+    assert O.capacity(8192, 8, 256, 1.2) == 308 and O.capacity(8192, 8, 256, 1.0) == 256
+    # hand example: three tokens, one expert, one row -> only token 0 is served
+    _, c1, _, m1, s1 = O.permute_capacity(np.eye(3), np.zeros((3, 1), np.int64), 1, 1)
+    assert list(m1[:, 0]) == [0, -1, -1] and list(s1) == [0] and c1[0] == 3
+
+
+def _small_layer(r, T=24, H=8, I=4, E=4, k=2, shared=True):
+    x = r.standard_normal((T, H))
+    w13 = r.standard_normal((E, 2 * I, H)) * 0.3
+    w2 = r.standard_normal((E, H, I)) * 0.3
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    ws13 = r.standard_normal((2 * I, H)) * 0.3 if shared else None
+    ws2 = r.standard_normal((H, I)) * 0.3 if shared else None
+    return x, w13, w2, logits, ws13, ws2
+
+
+def check_capacity_limits(O):
+    """A capacity of at least every count reduces to dropless (same outputs and
+    gradients); capacity 0 drops every pair (output = shared expert only, no
+    routed gradient, dgate 0)."""
+    r = np.random.default_rng(43)
+    T, k, E = 24, 2, 4
+    x, w13, w2, logits, ws13, ws2 = _small_layer(r, T=T, k=k, E=E)
+    dy = r.standard_normal(x.shape)
+    ref = O.layer_forward(x, k, E, w13, w2, logits=logits, ws13=ws13, ws2=ws2)
+    bref = O.layer_backward(ref, dy, x, w13, w2, ws13=ws13, ws2=ws2)
+    big = O.layer_forward(x, k, E, w13, w2, logits=logits, ws13=ws13, ws2=ws2, C=T)
+    bbig = O.layer_backward(big, dy, x, w13, w2, ws13=ws13, ws2=ws2)
+    assert np.allclose(big["y"], ref["y"], rtol=0, atol=1e-12)
+    for n in ("dx", "dw13", "dw2", "dgate", "dlogits"):
+        assert np.allclose(bbig[n], bref[n], rtol=0, atol=1e-12), n
+    # a capacity that drops some pairs: each token's output is the shared
+    # expert plus its served pairs only, each expert run on the token alone
+    mid = O.layer_forward(x, k, E, w13, w2, logits=logits, ws13=ws13, ws2=ws2, C=3)
+    rm, idx, gate = mid["row_id_map"], mid["idx"], mid["gate"]
+    assert (rm < 0).any() and (rm >= 0).any()
+    ys = O.expert_forward(x, ws13, ws2)[2]
+    for t in range(T):
+        want = ys[t].copy()
+        for j in range(k):
+            if rm[t, j] >= 0:
+                e = idx[t, j]
+                want += gate[t, j] * O.expert_forward(x[t:t + 1], w13[e], w2[e])[2][0]
+        assert np.allclose(mid["y"][t], want, rtol=0, atol=1e-12)
+    zero = O.layer_forward(x, k, E, w13, w2, logits=logits, ws13=ws13, ws2=ws2, C=0)
+    bz = O.layer_backward(zero, dy, x, w13, w2, ws13=ws13, ws2=ws2)
+    assert np.allclose(zero["y"], O.expert_forward(x, ws13, ws2)[2], rtol=0, atol=1e-12)
+    assert not bz["dgate"].any() and not bz["dw13"].any() and not bz["dw2"].any()
+    assert np.allclose(bz["dx"], O.expert_backward(x, ws13, ws2, dy)[1], rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
-    check_load_stats_closed_forms,
+    check_load_stats_closed_forms, check_capacity_bruteforce, check_capacity_limits,
     check_route_bruteforce, check_route_hand_example, check_gate_closed_forms,
     check_route_backward_fd, check_permute_invariants, check_identity_experts,
     check_expert_forward_bruteforce, check_dense_special_case, check_grouped_matches_per_group,

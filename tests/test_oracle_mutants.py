@@ -139,6 +139,28 @@ def _strided_groups(O):
     return load_stats
 
 
+def _drop_last_pairs(O):
+    orig = O.permute_capacity
+
+    def permute_capacity(x, idx, E, C):
+        # keeps each expert's last C pairs instead of its first C
+        T, k = idx.shape
+        xp, counts, offsets, rmap, src = orig(x[::-1], idx[::-1], E, C)
+        rmap = rmap[::-1].copy()
+        src = np.where(src >= 0, T - 1 - src, -1)
+        return x[np.maximum(src, 0)] * (src >= 0)[:, None], counts, offsets, rmap, src
+    return permute_capacity
+
+
+def _dropped_pairs_combine(O):
+    orig = O.combine
+
+    def combine(yp, rmap, gate, y_shared=None, acc=np.float64):
+        # a dropped pair (-1) is read as the last row
+        return orig(yp, np.where(rmap < 0, yp.shape[0] - 1, rmap), gate, y_shared, acc)
+    return combine
+
+
 MUTANTS = {
     "renormalised_gates": ("route", _renormalised_gates),
     "ties_to_higher_index": ("route", _ties_to_higher_index),
@@ -151,6 +173,8 @@ MUTANTS = {
     "dropped_shared": ("layer_forward", _dropped_shared),
     "sample_std_cv": ("load_stats", _sample_std_cv),
     "strided_groups": ("load_stats", _strided_groups),
+    "drop_last_pairs": ("permute_capacity", _drop_last_pairs),
+    "dropped_pairs_combine": ("combine", _dropped_pairs_combine),
 }
 
 
