@@ -27,7 +27,8 @@
  *  - Every call only enqueues work on ``stream`` (a hipStream_t; NULL is the
  *    null stream) and returns; none synchronises and none reads device data
  *    back to the host, so no output size depends on the routing: permuted
- *    buffers always have R = T*k rows (dropless, [Pangu-QA]).
+ *    buffers have R = T*k rows (dropless, [Pangu-QA]), or R = E*C in the
+ *    drop-and-pad variant (moe_permute_capacity).
  *  - The caller owns every buffer, including workspaces.  The library keeps no
  *    device memory; its only global state is the per-device CU count and the
  *    thread-local text of the last error.
@@ -38,8 +39,10 @@
  *    per tensor), MOE_ERR_WORKSPACE (workspace too small), MOE_ERR_LAUNCH (the
  *    runtime rejected a launch).  T == 0 is a successful no-op.  Device data
  *    is not checked: logits must be finite; offsets and row maps must come
- *    from moe_permute.  Kernels clamp every row index to its buffer, so bad
- *    device data gives wrong numbers, never an out-of-bounds access.
+ *    from moe_permute / moe_permute_capacity.  A row index outside [0, R)
+ *    stands for a dropped pair (reads as zeros, writes nothing); every other
+ *    index is clamped to its buffer, so bad device data gives wrong numbers,
+ *    never an out-of-bounds access.
  *  - Results are bitwise reproducible run to run (no floating-point atomics;
  *    every reduction has a fixed order).
  */
@@ -153,29 +156,58 @@ int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, 
 int moe_load_stats(const int32_t* counts, int E, int experts_per_group, float* load, float* cv,
                    int32_t* group_counts, moe_stream_t stream);
 
+/* Drop-and-pad permute, the variant the pages compare dropless training with
+ * ([CANN-MoE] s4.3 capacity factor 1.2; [Pangu-QA] MoE training analysis):
+ * every expert owns C rows, R = E*C (C = ceil(factor * T*k / E) for a
+ * capacity factor; any C >= 0 is accepted).
+ *   counts[e]       pairs routed to e, dropped or not                    [E]
+ *   offsets[e]      e*C                                                  [E+1]
+ *   row_id_map[t,j] e*C + rank if the pair's rank among e's pairs in token
+ *                   order is below C, else -1 (dropped)                  [T,k]
+ *   src_token[r]    token of row r, -1 for a row no pair fills           [E*C]
+ *   xp[r,:]         x[src_token[r],:], zeros for unfilled rows (nullable) [E*C,H]
+ * The grouped GEMMs then run on whole padded groups (offsets as above),
+ * combine and its backward skip dropped pairs, and the backward's dyp must
+ * have its unfilled rows cleared (moe_clear_empty_rows) so that padded rows
+ * stay exact zeros through dX and dW.  Same workspace as moe_permute.
+ */
+int moe_permute_capacity(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
+                         int C, void* xp, int32_t* counts, int32_t* offsets,
+                         int32_t* row_id_map, int32_t* src_token, void* ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
+/* buf[r,:] = 0 for every row r < R with src_token[r] < 0 (rows of a
+ * drop-and-pad buffer that no pair fills); other rows are untouched.
+ * buf is [R,H] of type dt. */
+int moe_clear_empty_rows(const int32_t* src_token, int R, int dt, int H, void* buf,
+                         moe_stream_t stream);
+
 /* Backward of the permute (adjoint of the row copy), fp32 sums:
  *   dx[t,:] = sum_j dxp[row_id_map[t,j],:] + add0[t,:] + add1[t,:]
  * add0/add1 are optional [T,H] tensors of type dt (nullable), e.g. the shared
- * expert's and the router's input gradients.  dx is written.
+ * expert's and the router's input gradients.  dx is written.  dxp has R rows
+ * (T*k dropless, E*C drop-and-pad); a dropped pair adds nothing.
  */
 int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int dt, int T, int H, int k,
-                    const void* add0, const void* add1, void* dx, moe_stream_t stream);
+                    int R, const void* add0, const void* add1, void* dx, moe_stream_t stream);
 
 /* Anti-reorder and gate-weighted combine ([MoE-ops] VectorSort; [Pangu-QA]
  * experimental results; the shared expert enters with weight 1):
  *   y[t,:] = y_shared[t,:] + sum_{j=0..k-1} gate[t,j] * yp[row_id_map[t,j],:]
- * summed in fp32 in ascending j; y_shared nullable.
+ * summed in fp32 in ascending j; y_shared nullable.  yp has R rows; a
+ * dropped pair (drop-and-pad) adds nothing.
  */
 int moe_unpermute_combine(const void* yp, const int32_t* row_id_map, const float* gate,
-                          const void* y_shared, int dt, int T, int H, int k, void* y,
+                          const void* y_shared, int dt, int T, int H, int k, int R, void* y,
                           moe_stream_t stream);
 
 /* Backward of moe_unpermute_combine:
- *   dyp[row_id_map[t,j],:] = gate[t,j] * dy[t,:]          (all T*k rows written)
+ *   dyp[row_id_map[t,j],:] = gate[t,j] * dy[t,:]          (every pair's row written)
  *   dgate[t,j]             = <dy[t,:], yp[row_id_map[t,j],:]>   (fp32)
+ * yp and dyp have R rows; a dropped pair writes no row and gets dgate 0.
  */
 int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row_id_map,
-                              const float* gate, int dt, int T, int H, int k, void* dyp,
+                              const float* gate, int dt, int T, int H, int k, int R, void* dyp,
                               float* dgate, moe_stream_t stream);
 
 /* ---------------------------------------------------------------- grouped GEMM

@@ -54,9 +54,12 @@ _SIGS = {
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_load_stats": (_I, [_P, _I, _I, _P, _P, _P, _P]),
-    "moe_permute_bwd": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
-    "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
-    "moe_unpermute_combine_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_permute_capacity": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                  _P]),
+    "moe_clear_empty_rows": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_permute_bwd": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_unpermute_combine_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_gmm_workspace_bytes": (_SZ, []),
     "moe_grouped_gemm_fwd": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                   ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
@@ -162,19 +165,29 @@ def moe_load_stats(counts, E, experts_per_group, load, cv, group_counts, stream=
           addr(group_counts), _stream(stream))
 
 
-def moe_permute_bwd(dxp, row_id_map, dt, T, H, k, add0, add1, dx, stream=None):
-    _call("moe_permute_bwd", addr(dxp), addr(row_id_map), dt, T, H, k, addr(add0), addr(add1),
+def moe_permute_capacity(x, dt, idx, T, H, E, k, C, xp, counts, offsets, row_id_map,
+                         src_token, ws, ws_bytes, stream=None):
+    _call("moe_permute_capacity", addr(x), dt, addr(idx), T, H, E, k, C, addr(xp), addr(counts),
+          addr(offsets), addr(row_id_map), addr(src_token), addr(ws), ws_bytes, _stream(stream))
+
+
+def moe_clear_empty_rows(src_token, R, dt, H, buf, stream=None):
+    _call("moe_clear_empty_rows", addr(src_token), R, dt, H, addr(buf), _stream(stream))
+
+
+def moe_permute_bwd(dxp, row_id_map, dt, T, H, k, R, add0, add1, dx, stream=None):
+    _call("moe_permute_bwd", addr(dxp), addr(row_id_map), dt, T, H, k, R, addr(add0), addr(add1),
           addr(dx), _stream(stream))
 
 
-def moe_unpermute_combine(yp, row_id_map, gate, y_shared, dt, T, H, k, y, stream=None):
+def moe_unpermute_combine(yp, row_id_map, gate, y_shared, dt, T, H, k, R, y, stream=None):
     _call("moe_unpermute_combine", addr(yp), addr(row_id_map), addr(gate), addr(y_shared), dt,
-          T, H, k, addr(y), _stream(stream))
+          T, H, k, R, addr(y), _stream(stream))
 
 
-def moe_unpermute_combine_bwd(dy, yp, row_id_map, gate, dt, T, H, k, dyp, dgate, stream=None):
+def moe_unpermute_combine_bwd(dy, yp, row_id_map, gate, dt, T, H, k, R, dyp, dgate, stream=None):
     _call("moe_unpermute_combine_bwd", addr(dy), addr(yp), addr(row_id_map), addr(gate), dt, T,
-          H, k, addr(dyp), addr(dgate), _stream(stream))
+          H, k, R, addr(dyp), addr(dgate), _stream(stream))
 
 
 def shared_expert(T=0, **tensors) -> SharedExpert:

@@ -20,6 +20,18 @@
 
 static inline long long perm_chunks(int T) { return (T + PERM_CHUNK - 1) / PERM_CHUNK; }
 
+// Byte offset of a row that is not there (a dropped pair, or a row index
+// outside [0, R)): every permuted-row buffer's descriptor stops at or before
+// ROW_DROP bytes, so loads from it read zero and stores to it are discarded.
+#define ROW_DROP 0xFFFF0000u
+__device__ __forceinline__ uint32_t row_off(long long row, long long R, uint32_t row_bytes) {
+  return (row >= 0 && row < R) ? (uint32_t)row * row_bytes : ROW_DROP;
+}
+__host__ __device__ __forceinline__ uint32_t rows_bytes(long long R, uint32_t row_bytes) {
+  const long long b = R * (long long)row_bytes;
+  return b <= 0 ? 0u : (b >= (long long)ROW_DROP ? ROW_DROP : (uint32_t)b);
+}
+
 // ---------------------------------------------------------------- rank
 
 __global__ __launch_bounds__(MOE_WAVE) void permute_rank_kernel(
@@ -168,31 +180,44 @@ __global__ __launch_bounds__(1024) void load_stats_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------- scatter
 
+// Row of pair p = (t, j) of chunk c: its stable rank inside expert e is the
+// chunk's base plus the local rank (held in row_id_map until now).  Dropless
+// (cap < 0): row = offsets[e] + rank.  Drop-and-pad (cap >= 0, offsets[e] =
+// e * cap): the pair keeps that row if rank < cap, else it is dropped (-1).
+__device__ __forceinline__ long long pair_row(const int32_t* __restrict__ idx,
+                                              const int32_t* __restrict__ offsets,
+                                              const int32_t* __restrict__ hist,
+                                              const int32_t* __restrict__ row_id_map, long long p,
+                                              int c, int E, int cap, long long R) {
+  int e = idx[p];
+  e = (e >= 0 && e < E) ? e : 0;
+  const long long rank = (long long)hist[(long long)c * E + e] + row_id_map[p];
+  if (cap >= 0 && rank >= cap) return -1;
+  long long row = (long long)offsets[e] + rank;
+  return row < 0 ? 0 : (row >= R ? R - 1 : row);
+}
+
 template <int ESZ>
 __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ hist, int T, int H, int E,
-    int k, void* __restrict__ xp, int32_t* __restrict__ row_id_map,
+    int k, int cap, long long R, void* __restrict__ xp, int32_t* __restrict__ row_id_map,
     int32_t* __restrict__ src_token) {
-  __shared__ int rows[MOE_MAX_E];
+  __shared__ uint32_t rofs[MOE_MAX_E];
   const int t = blockIdx.x;
-  const long long R = (long long)T * k;
   const int c = t / PERM_CHUNK;
+  const uint32_t row_bytes = (uint32_t)H * ESZ;
   for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
-    long long p = (long long)t * k + j;
-    int e = idx[p];
-    e = (e >= 0 && e < E) ? e : 0;
-    long long row = (long long)offsets[e] + hist[(long long)c * E + e] + row_id_map[p];
-    row = row < 0 ? 0 : (row >= R ? R - 1 : row);
+    const long long p = (long long)t * k + j;
+    const long long row = pair_row(idx, offsets, hist, row_id_map, p, c, E, cap, R);
     row_id_map[p] = (int)row;
-    src_token[row] = t;
-    rows[j] = (int)row;
+    if (row >= 0) src_token[row] = t;
+    rofs[j] = row_off(row, R, row_bytes);
   }
   __syncthreads();
-  const uint32_t row_bytes = (uint32_t)H * ESZ;
   const int nchunk = row_bytes / 16;
   __amdgpu_buffer_rsrc_t src = make_rsrc((const char*)x + (long long)t * row_bytes, row_bytes);
-  __amdgpu_buffer_rsrc_t dst = make_rsrc(xp, clamp_bytes(R * row_bytes));
+  __amdgpu_buffer_rsrc_t dst = make_rsrc(xp, rows_bytes(R, row_bytes));
   for (int q0 = 0; q0 < nchunk; q0 += ROW_THREADS * ROW_MAXC) {
     u32x4 v[ROW_MAXC];
 #pragma unroll
@@ -201,7 +226,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
       v[i] = buf_load16_nt(src, (uint32_t)q * 16u);
     }
     for (int j = 0; j < k; ++j) {
-      const uint32_t rb = (uint32_t)rows[j] * row_bytes;
+      const uint32_t rb = rofs[j];
 #pragma unroll
       for (int i = 0; i < ROW_MAXC; ++i) {
         int q = q0 + i * ROW_THREADS + threadIdx.x;
@@ -214,19 +239,54 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
 // Row map and source tokens only (no row copy): one thread per (t, j).
 __global__ __launch_bounds__(256) void permute_maps_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ hist, int T, int E, int k, int32_t* __restrict__ row_id_map,
-    int32_t* __restrict__ src_token) {
-  const long long R = (long long)T * k;
+    const int32_t* __restrict__ hist, int T, int E, int k, int cap, long long R,
+    int32_t* __restrict__ row_id_map, int32_t* __restrict__ src_token) {
   const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (p >= R) return;
+  if (p >= (long long)T * k) return;
   const int t = (int)(p / k);
-  const int c = t / PERM_CHUNK;
-  int e = idx[p];
-  e = (e >= 0 && e < E) ? e : 0;
-  long long row = (long long)offsets[e] + hist[(long long)c * E + e] + row_id_map[p];
-  row = row < 0 ? 0 : (row >= R ? R - 1 : row);
+  const long long row = pair_row(idx, offsets, hist, row_id_map, p, t / PERM_CHUNK, E, cap, R);
   row_id_map[p] = (int)row;
-  src_token[row] = t;
+  if (row >= 0) src_token[row] = t;
+}
+
+// Drop-and-pad: offsets[e] = e * C (e = 0..E).
+__global__ __launch_bounds__(1024) void permute_cap_offsets_kernel(int32_t* __restrict__ offsets,
+                                                                   int E, int C) {
+  for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = e * C;
+}
+
+// Drop-and-pad: the rows [e*C + counts[e], (e+1)*C) that no pair fills get
+// src_token = -1 (and zeros in xp when given).  Grid-stride over rows, one
+// row per workgroup and pass.
+template <int ESZ>
+__global__ __launch_bounds__(ROW_THREADS) void permute_pad_kernel(
+    const int32_t* __restrict__ counts, int E, int C, int H, void* __restrict__ xp,
+    int32_t* __restrict__ src_token) {
+  const long long R = (long long)E * C;
+  const uint32_t row_bytes = (uint32_t)H * ESZ;
+  const int nchunk = row_bytes / 16;
+  __amdgpu_buffer_rsrc_t dst = make_rsrc(xp, xp ? rows_bytes(R, row_bytes) : 0u);
+  for (long long r = blockIdx.x; r < R; r += gridDim.x) {
+    const int e = (int)(r / C), n = (int)(r % C);
+    if (n < counts[e]) continue;   // uniform: a filled row
+    if (threadIdx.x == 0) src_token[r] = -1;
+    if (xp)
+      for (int q = threadIdx.x; q < nchunk; q += ROW_THREADS)
+        buf_store16(dst, (uint32_t)r * row_bytes + (uint32_t)q * 16u, u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// buf[r, :] = 0 for every row r < R with src_token[r] < 0 (a row no pair
+// fills).  Grid-stride over rows, one row per workgroup and pass.
+__global__ __launch_bounds__(ROW_THREADS) void clear_empty_rows_kernel(
+    const int32_t* __restrict__ src_token, long long R, uint32_t row_bytes, void* __restrict__ buf) {
+  const int nchunk = row_bytes / 16;
+  __amdgpu_buffer_rsrc_t dst = make_rsrc(buf, rows_bytes(R, row_bytes));
+  for (long long r = blockIdx.x; r < R; r += gridDim.x) {
+    if (src_token[r] >= 0) continue;   // uniform
+    for (int q = threadIdx.x; q < nchunk; q += ROW_THREADS)
+      buf_store16(dst, (uint32_t)r * row_bytes + (uint32_t)q * 16u, u32x4{0u, 0u, 0u, 0u});
+  }
 }
 
 // ---------------------------------------------------------------- gathers
@@ -251,19 +311,16 @@ __device__ __forceinline__ u32x4 row_chunk(const __amdgpu_buffer_rsrc_t& rs, uin
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
     const T* __restrict__ dxp, const int32_t* __restrict__ row_id_map, int Tn, int H, int k,
-    const T* __restrict__ add0, const T* __restrict__ add1, T* __restrict__ dx) {
+    long long R, const T* __restrict__ add0, const T* __restrict__ add1, T* __restrict__ dx) {
   constexpr int VEC = Elem<T>::VEC;
-  __shared__ int rows[MOE_MAX_E];
+  __shared__ uint32_t rofs[MOE_MAX_E];
   const int t = blockIdx.x;
-  const long long R = (long long)Tn * k;
-  for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
-    long long row = row_id_map[(long long)t * k + j];
-    rows[j] = (int)(row < 0 ? 0 : (row >= R ? R - 1 : row));
-  }
-  __syncthreads();
   const uint32_t row_bytes = (uint32_t)H * sizeof(T);
+  for (int j = threadIdx.x; j < k; j += ROW_THREADS)
+    rofs[j] = row_off(row_id_map[(long long)t * k + j], R, row_bytes);
+  __syncthreads();
   const int nchunk = row_bytes / 16;
-  __amdgpu_buffer_rsrc_t src = make_rsrc(dxp, clamp_bytes(R * row_bytes));
+  __amdgpu_buffer_rsrc_t src = make_rsrc(dxp, rows_bytes(R, row_bytes));
   __amdgpu_buffer_rsrc_t out = make_rsrc((char*)dx + (long long)t * row_bytes, row_bytes);
   __amdgpu_buffer_rsrc_t a0 = make_rsrc(add0 ? (const char*)add0 + (long long)t * row_bytes : nullptr,
                                         add0 ? row_bytes : 0);
@@ -280,7 +337,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
 #pragma unroll
       for (int jj = 0; jj < ROW_JB; ++jj)
         if (j0 + jj < k) {
-          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+          const uint32_t rb = rofs[j0 + jj];
 #pragma unroll
           for (int u = 0; u < ROW_QB; ++u) v[jj][u] = row_chunk(src, rb, q0 + u * ROW_THREADS, nchunk);
         }
@@ -325,22 +382,23 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
     const T* __restrict__ yp, const int32_t* __restrict__ row_id_map,
-    const float* __restrict__ gate, const T* __restrict__ ys, int Tn, int H, int k,
+    const float* __restrict__ gate, const T* __restrict__ ys, int Tn, int H, int k, long long R,
     T* __restrict__ y) {
   constexpr int VEC = Elem<T>::VEC;
-  __shared__ int rows[MOE_MAX_E];
+  __shared__ uint32_t rofs[MOE_MAX_E];
   __shared__ float gates[MOE_MAX_E];
   const int t = blockIdx.x;
-  const long long R = (long long)Tn * k;
+  const uint32_t row_bytes = (uint32_t)H * sizeof(T);
   for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
-    long long row = row_id_map[(long long)t * k + j];
-    rows[j] = (int)(row < 0 ? 0 : (row >= R ? R - 1 : row));
-    gates[j] = gate[(long long)t * k + j];
+    const long long row = row_id_map[(long long)t * k + j];
+    rofs[j] = row_off(row, R, row_bytes);
+    // a dropped pair adds nothing (its row reads as zeros; the gate is
+    // cleared too so that a non-finite gate cannot leak in)
+    gates[j] = (row >= 0 && row < R) ? gate[(long long)t * k + j] : 0.f;
   }
   __syncthreads();
-  const uint32_t row_bytes = (uint32_t)H * sizeof(T);
   const int nchunk = row_bytes / 16;
-  __amdgpu_buffer_rsrc_t src = make_rsrc(yp, clamp_bytes(R * row_bytes));
+  __amdgpu_buffer_rsrc_t src = make_rsrc(yp, rows_bytes(R, row_bytes));
   __amdgpu_buffer_rsrc_t out = make_rsrc((char*)y + (long long)t * row_bytes, row_bytes);
   __amdgpu_buffer_rsrc_t sh = make_rsrc(ys ? (const char*)ys + (long long)t * row_bytes : nullptr,
                                         ys ? row_bytes : 0);
@@ -360,7 +418,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
 #pragma unroll
       for (int jj = 0; jj < ROW_JB; ++jj)
         if (j0 + jj < k) {
-          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+          const uint32_t rb = rofs[j0 + jj];
 #pragma unroll
           for (int u = 0; u < ROW_QB; ++u) v[jj][u] = row_chunk(src, rb, q0 + u * ROW_THREADS, nchunk);
         }
@@ -390,26 +448,26 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ yp, const int32_t* __restrict__ row_id_map,
-    const float* __restrict__ gate, int Tn, int H, int k, T* __restrict__ dyp,
+    const float* __restrict__ gate, int Tn, int H, int k, long long R, T* __restrict__ dyp,
     float* __restrict__ dgate) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int NW = ROW_THREADS / MOE_WAVE;
-  __shared__ int rows[MOE_MAX_E];
+  __shared__ uint32_t rofs[MOE_MAX_E];
   __shared__ float gates[MOE_MAX_E];
   __shared__ float red[ROW_JB][NW];
   const int t = blockIdx.x;
-  const long long R = (long long)Tn * k;
+  const uint32_t row_bytes = (uint32_t)H * sizeof(T);
   for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
-    long long row = row_id_map[(long long)t * k + j];
-    rows[j] = (int)(row < 0 ? 0 : (row >= R ? R - 1 : row));
+    // a dropped pair: no dyp row (the stores go past the buffer) and
+    // dgate = <dy, 0> = 0
+    rofs[j] = row_off(row_id_map[(long long)t * k + j], R, row_bytes);
     gates[j] = gate[(long long)t * k + j];
   }
   __syncthreads();
-  const uint32_t row_bytes = (uint32_t)H * sizeof(T);
   const int nchunk = row_bytes / 16;
   __amdgpu_buffer_rsrc_t din = make_rsrc((const char*)dy + (long long)t * row_bytes, row_bytes);
-  __amdgpu_buffer_rsrc_t ypr = make_rsrc(yp, clamp_bytes(R * row_bytes));
-  __amdgpu_buffer_rsrc_t dst = make_rsrc(dyp, clamp_bytes(R * row_bytes));
+  __amdgpu_buffer_rsrc_t ypr = make_rsrc(yp, rows_bytes(R, row_bytes));
+  __amdgpu_buffer_rsrc_t dst = make_rsrc(dyp, rows_bytes(R, row_bytes));
   const int lane = threadIdx.x % MOE_WAVE, w = threadIdx.x / MOE_WAVE;
   // the token's dy row stays in registers (ROW_MAXC chunks per thread)
   u32x4 draw[ROW_MAXC];
@@ -427,7 +485,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
 #pragma unroll
       for (int jj = 0; jj < ROW_JB; ++jj)
         if (j0 + jj < k) {
-          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+          const uint32_t rb = rofs[j0 + jj];
 #pragma unroll
           for (int u = 0; u < ROW_QB; ++u)
             v[jj][u] = row_chunk(ypr, rb, threadIdx.x + (c0 + u) * ROW_THREADS, nchunk);
@@ -435,7 +493,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
 #pragma unroll
       for (int jj = 0; jj < ROW_JB; ++jj)
         if (j0 + jj < k) {
-          const uint32_t rb = (uint32_t)rows[j0 + jj] * row_bytes;
+          const uint32_t rb = rofs[j0 + jj];
           const float g = gates[j0 + jj];
 #pragma unroll
           for (int u = 0; u < ROW_QB; ++u) {
@@ -480,7 +538,16 @@ static int row_checks(const char* fn, int dt, int T, int H, int k) {
   if (row_bytes > 16LL * ROW_THREADS * ROW_MAXC)
     return moe_fail(MOE_ERR_UNSUPPORTED, "%s: a row of H = %d elements exceeds %d bytes", fn, H,
                     16 * ROW_THREADS * ROW_MAXC);
-  MOE_TRY(moe_need_elems((long long)T * k, H, moe_dt_bytes(dt), fn, "permuted rows"));
+  return MOE_OK;
+}
+
+// R permuted rows of H elements: addressable below ROW_DROP bytes
+static int perm_rows_check(const char* fn, int dt, long long R, int H) {
+  if (R < 0) return moe_fail(MOE_ERR_INVALID_ARG, "%s: R = %lld is negative", fn, R);
+  MOE_TRY(moe_need_elems(R, H, moe_dt_bytes(dt), fn, "permuted rows"));
+  if (R * H * moe_dt_bytes(dt) > (long long)ROW_DROP)
+    return moe_fail(MOE_ERR_UNSUPPORTED, "%s: %lld permuted rows of %d elements exceed %u bytes",
+                    fn, R, H, ROW_DROP);
   return MOE_OK;
 }
 
@@ -490,52 +557,108 @@ extern "C" size_t moe_permute_workspace_bytes(int T, int E, int k) {
   return (size_t)perm_chunks(T) * (size_t)E * sizeof(int32_t);
 }
 
-extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
-                           void* xp, int32_t* counts, int32_t* offsets, int32_t* row_id_map,
-                           int32_t* src_token, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  const char* fn = "moe_permute";
+// Dropless (cap < 0, R = T*k) or drop-and-pad (cap = C >= 0, R = E*C).
+static int permute_impl(const char* fn, const void* x, int dt, const int32_t* idx, int T, int H,
+                        int E, int k, int cap, void* xp, int32_t* counts, int32_t* offsets,
+                        int32_t* row_id_map, int32_t* src_token, void* ws, size_t ws_bytes,
+                        moe_stream_t stream) {
   MOE_TRY(row_checks(fn, dt, T, H, k));
   MOE_TRY(moe_need_ek(E, k, fn));
+  const long long R = cap < 0 ? (long long)T * k : (long long)E * cap;
+  MOE_TRY(perm_rows_check(fn, dt, R, H));
   MOE_TRY(moe_need_ptr(counts, fn, "counts", 4));
   MOE_TRY(moe_need_ptr(offsets, fn, "offsets", 4));
+  MOE_TRY((xp && T > 0) ? moe_need_ptr(x, fn, "x") : moe_opt_ptr(x, fn, "x"));
+  MOE_TRY(moe_opt_ptr(xp, fn, "xp"));
+  if (T > 0) {
+    MOE_TRY(moe_need_ptr(idx, fn, "idx", 4));
+    MOE_TRY(moe_need_ptr(row_id_map, fn, "row_id_map", 4));
+    MOE_TRY(moe_need_ptr(ws, fn, "ws", 4));
+    if (ws_bytes < moe_permute_workspace_bytes(T, E, k))
+      return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
+                      moe_permute_workspace_bytes(T, E, k));
+  }
+  if (R > 0) MOE_TRY(moe_need_ptr(src_token, fn, "src_token", 4));
   hipStream_t s = (hipStream_t)stream;
+  int32_t* hist = (int32_t*)ws;
   if (T == 0) {
     // empty input: every group is empty (a fill kernel, not a memset node)
     hipLaunchKernelGGL(permute_zero_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E);
-    return moe_check_launch("moe_permute(empty)");
+    MOE_TRY(moe_check_launch(fn));
+  } else {
+    const int nchunks = (int)perm_chunks(T);
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(MOE_WAVE), 0, s, idx, T, E, k,
+                       row_id_map, hist);
+    MOE_TRY(moe_check_launch(fn));
+    hipLaunchKernelGGL(permute_colscan_kernel, dim3((E + MOE_WAVE - 1) / MOE_WAVE),
+                       dim3(MOE_WAVE * SCAN_SLICES), 0, s, hist, nchunks, E, counts);
+    MOE_TRY(moe_check_launch(fn));
   }
-  MOE_TRY(xp ? moe_need_ptr(x, fn, "x") : moe_opt_ptr(x, fn, "x"));
-  MOE_TRY(moe_need_ptr(idx, fn, "idx", 4));
-  MOE_TRY(moe_opt_ptr(xp, fn, "xp"));
-  MOE_TRY(moe_need_ptr(row_id_map, fn, "row_id_map", 4));
+  if (cap < 0) {
+    if (T > 0) hipLaunchKernelGGL(permute_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E,
+                                  offsets);
+  } else {
+    hipLaunchKernelGGL(permute_cap_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, cap);
+  }
+  MOE_TRY(moe_check_launch(fn));
+  if (T > 0) {
+    if (xp == nullptr) {
+      const long long P = (long long)T * k;
+      hipLaunchKernelGGL(permute_maps_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s,
+                         idx, offsets, hist, T, E, k, cap, R, row_id_map, src_token);
+    } else if (dt == MOE_BF16) {
+      hipLaunchKernelGGL(permute_scatter_kernel<2>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
+                         offsets, hist, T, H, E, k, cap, R, xp, row_id_map, src_token);
+    } else {
+      hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
+                         offsets, hist, T, H, E, k, cap, R, xp, row_id_map, src_token);
+    }
+    MOE_TRY(moe_check_launch(fn));
+  }
+  if (cap > 0) {
+    const unsigned grid = (unsigned)(R < 4096 ? R : 4096);
+    if (dt == MOE_BF16)
+      hipLaunchKernelGGL(permute_pad_kernel<2>, dim3(grid), dim3(ROW_THREADS), 0, s, counts, E,
+                         cap, H, xp, src_token);
+    else
+      hipLaunchKernelGGL(permute_pad_kernel<4>, dim3(grid), dim3(ROW_THREADS), 0, s, counts, E,
+                         cap, H, xp, src_token);
+    MOE_TRY(moe_check_launch(fn));
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
+                           void* xp, int32_t* counts, int32_t* offsets, int32_t* row_id_map,
+                           int32_t* src_token, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return permute_impl("moe_permute", x, dt, idx, T, H, E, k, -1, xp, counts, offsets, row_id_map,
+                      src_token, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_permute_capacity(const void* x, int dt, const int32_t* idx, int T, int H, int E,
+                                    int k, int C, void* xp, int32_t* counts, int32_t* offsets,
+                                    int32_t* row_id_map, int32_t* src_token, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream) {
+  const char* fn = "moe_permute_capacity";
+  if (C < 0) return moe_fail(MOE_ERR_INVALID_ARG, "%s: C = %d is negative", fn, C);
+  return permute_impl(fn, x, dt, idx, T, H, E, k, C, xp, counts, offsets, row_id_map, src_token,
+                      ws, ws_bytes, stream);
+}
+
+extern "C" int moe_clear_empty_rows(const int32_t* src_token, int R, int dt, int H, void* buf,
+                                    moe_stream_t stream) {
+  const char* fn = "moe_clear_empty_rows";
+  MOE_TRY(moe_need_dt(dt, fn));
+  MOE_TRY(moe_need_mult64(H, fn, "H"));
+  MOE_TRY(perm_rows_check(fn, dt, R, H));
+  if (R == 0) return MOE_OK;
   MOE_TRY(moe_need_ptr(src_token, fn, "src_token", 4));
-  MOE_TRY(moe_need_ptr(ws, fn, "ws", 4));
-  if (ws_bytes < moe_permute_workspace_bytes(T, E, k))
-    return moe_fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
-                    moe_permute_workspace_bytes(T, E, k));
-  const int nchunks = (int)perm_chunks(T);
-  int32_t* hist = (int32_t*)ws;
-  hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(MOE_WAVE), 0, s, idx, T, E, k,
-                     row_id_map, hist);
-  MOE_TRY(moe_check_launch("moe_permute(rank)"));
-  hipLaunchKernelGGL(permute_colscan_kernel, dim3((E + MOE_WAVE - 1) / MOE_WAVE),
-                     dim3(MOE_WAVE * SCAN_SLICES), 0, s, hist, nchunks, E, counts);
-  MOE_TRY(moe_check_launch("moe_permute(scan)"));
-  hipLaunchKernelGGL(permute_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E, offsets);
-  MOE_TRY(moe_check_launch("moe_permute(offsets)"));
-  if (xp == nullptr) {
-    const long long R = (long long)T * k;
-    hipLaunchKernelGGL(permute_maps_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
-                       idx, offsets, hist, T, E, k, row_id_map, src_token);
-    return moe_check_launch("moe_permute(maps)");
-  }
-  if (dt == MOE_BF16)
-    hipLaunchKernelGGL(permute_scatter_kernel<2>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
-                       offsets, hist, T, H, E, k, xp, row_id_map, src_token);
-  else
-    hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
-                       offsets, hist, T, H, E, k, xp, row_id_map, src_token);
-  return moe_check_launch("moe_permute(scatter)");
+  MOE_TRY(moe_need_ptr(buf, fn, "buf"));
+  const unsigned grid = (unsigned)(R < 4096 ? R : 4096);
+  hipLaunchKernelGGL(clear_empty_rows_kernel, dim3(grid), dim3(ROW_THREADS), 0,
+                     (hipStream_t)stream, src_token, (long long)R,
+                     (uint32_t)(H * moe_dt_bytes(dt)), buf);
+  return moe_check_launch(fn);
 }
 
 extern "C" int moe_load_stats(const int32_t* counts, int E, int experts_per_group, float* load,
@@ -556,10 +679,11 @@ extern "C" int moe_load_stats(const int32_t* counts, int E, int experts_per_grou
 }
 
 extern "C" int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int dt, int T, int H,
-                               int k, const void* add0, const void* add1, void* dx,
+                               int k, int R, const void* add0, const void* add1, void* dx,
                                moe_stream_t stream) {
   const char* fn = "moe_permute_bwd";
   MOE_TRY(row_checks(fn, dt, T, H, k));
+  MOE_TRY(perm_rows_check(fn, dt, R, H));
   if (T == 0) return MOE_OK;
   MOE_TRY(moe_need_ptr(dxp, fn, "dxp"));
   MOE_TRY(moe_need_ptr(row_id_map, fn, "row_id_map", 4));
@@ -569,20 +693,21 @@ extern "C" int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int d
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const bf16_t*)dxp, row_id_map, T, H, k, (const bf16_t*)add0,
+                       (const bf16_t*)dxp, row_id_map, T, H, k, (long long)R, (const bf16_t*)add0,
                        (const bf16_t*)add1, (bf16_t*)dx);
   else
     hipLaunchKernelGGL(permute_bwd_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const float*)dxp, row_id_map, T, H, k, (const float*)add0,
+                       (const float*)dxp, row_id_map, T, H, k, (long long)R, (const float*)add0,
                        (const float*)add1, (float*)dx);
   return moe_check_launch(fn);
 }
 
 extern "C" int moe_unpermute_combine(const void* yp, const int32_t* row_id_map, const float* gate,
-                                     const void* y_shared, int dt, int T, int H, int k, void* y,
-                                     moe_stream_t stream) {
+                                     const void* y_shared, int dt, int T, int H, int k, int R,
+                                     void* y, moe_stream_t stream) {
   const char* fn = "moe_unpermute_combine";
   MOE_TRY(row_checks(fn, dt, T, H, k));
+  MOE_TRY(perm_rows_check(fn, dt, R, H));
   if (T == 0) return MOE_OK;
   MOE_TRY(moe_need_ptr(yp, fn, "yp"));
   MOE_TRY(moe_need_ptr(row_id_map, fn, "row_id_map", 4));
@@ -593,18 +718,20 @@ extern "C" int moe_unpermute_combine(const void* yp, const int32_t* row_id_map, 
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
                        (const bf16_t*)yp, row_id_map, gate, (const bf16_t*)y_shared, T, H, k,
-                       (bf16_t*)y);
+                       (long long)R, (bf16_t*)y);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s, (const float*)yp,
-                       row_id_map, gate, (const float*)y_shared, T, H, k, (float*)y);
+                       row_id_map, gate, (const float*)y_shared, T, H, k, (long long)R,
+                       (float*)y);
   return moe_check_launch(fn);
 }
 
 extern "C" int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row_id_map,
-                                         const float* gate, int dt, int T, int H, int k, void* dyp,
-                                         float* dgate, moe_stream_t stream) {
+                                         const float* gate, int dt, int T, int H, int k, int R,
+                                         void* dyp, float* dgate, moe_stream_t stream) {
   const char* fn = "moe_unpermute_combine_bwd";
   MOE_TRY(row_checks(fn, dt, T, H, k));
+  MOE_TRY(perm_rows_check(fn, dt, R, H));
   if (T == 0) return MOE_OK;
   MOE_TRY(moe_need_ptr(dy, fn, "dy"));
   MOE_TRY(moe_need_ptr(yp, fn, "yp"));
@@ -616,10 +743,10 @@ extern "C" int moe_unpermute_combine_bwd(const void* dy, const void* yp, const i
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
                        (const bf16_t*)dy, (const bf16_t*)yp, row_id_map, gate, T, H, k,
-                       (bf16_t*)dyp, dgate);
+                       (long long)R, (bf16_t*)dyp, dgate);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s,
                        (const float*)dy, (const float*)yp, row_id_map, gate, T, H, k,
-                       (float*)dyp, dgate);
+                       (long long)R, (float*)dyp, dgate);
   return moe_check_launch(fn);
 }

@@ -17,6 +17,11 @@ its tiles from per-XCD counters, so whichever kernel holds fewer CUs at the
 end of another one's last round simply takes fewer tiles; results are
 bitwise identical to the sequential order.
 
+With ``shape.capacity`` = C the layer is the drop-and-pad variant: every
+expert owns C rows, pairs past an expert's first C (in token order) are
+dropped, unfilled rows are zero, and the grouped GEMM runs on the padded
+groups.
+
 Experts outside ``[g0, g0+G)`` are remote: their rows are moved by the
 permute and the combine, their expert outputs and input gradients are zero
 (the buffers are cleared once at allocation and never written), and they get
@@ -44,6 +49,7 @@ class LayerShape:
     G: Optional[int] = None     # experts run by the grouped GEMM (None = all E)
     shared: bool = False
     router: bool = True         # False: logits are an input
+    capacity: Optional[int] = None   # drop-and-pad: rows per expert (None = dropless)
 
     @property
     def groups(self) -> int:
@@ -51,7 +57,8 @@ class LayerShape:
 
     @property
     def R(self) -> int:
-        return self.T * self.k
+        """Rows of the permuted buffers."""
+        return self.T * self.k if self.capacity is None else self.E * self.capacity
 
 
 class MoeLayer:
@@ -161,6 +168,11 @@ class MoeLayer:
 
     def permute(self, stream=None):
         s = self.s
+        if s.capacity is not None:
+            abi.moe_permute_capacity(self.x, self.dt, self.idx, s.T, s.H, s.E, s.k, s.capacity,
+                                     self.xp, self.counts, self.offsets, self.row_id_map,
+                                     self.src_token, self.ws, self.ws_bytes, stream)
+            return
         abi.moe_permute(self.x, self.dt, self.idx, s.T, s.H, s.E, s.k, self.xp, self.counts,
                         self.offsets, self.row_id_map, self.src_token, self.ws, self.ws_bytes,
                         stream)
@@ -204,13 +216,15 @@ class MoeLayer:
     def combine(self, stream=None):
         s = self.s
         abi.moe_unpermute_combine(self.yp, self.row_id_map, self.gate,
-                                  self.ys if s.shared else None, self.dt, s.T, s.H, s.k, self.y,
-                                  stream)
+                                  self.ys if s.shared else None, self.dt, s.T, s.H, s.k, s.R,
+                                  self.y, stream)
 
     def combine_bwd(self, stream=None):
         s = self.s
         abi.moe_unpermute_combine_bwd(self.dy, self.yp, self.row_id_map, self.gate, self.dt, s.T,
-                                      s.H, s.k, self.dyp, self.dgate, stream)
+                                      s.H, s.k, s.R, self.dyp, self.dgate, stream)
+        if s.capacity is not None:   # padded rows of dyp: exact zeros through dX and dW
+            abi.moe_clear_empty_rows(self.src_token, s.R, self.dt, s.H, self.dyp, stream)
 
     def gmm_bwd_dx(self, stream=None, part="all"):
         s = self.s
@@ -244,7 +258,7 @@ class MoeLayer:
 
     def permute_bwd(self, stream=None):
         s = self.s
-        abi.moe_permute_bwd(self.dxp, self.row_id_map, self.dt, s.T, s.H, s.k,
+        abi.moe_permute_bwd(self.dxp, self.row_id_map, self.dt, s.T, s.H, s.k, s.R,
                             self.sh_dx if s.shared else None,
                             self.dx_router if s.router else None, self.dx, stream)
 

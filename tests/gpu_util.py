@@ -39,16 +39,17 @@ def rel_err(gpu, ref) -> float:
     return float(diff / scale)
 
 
-def shape_of(cfg: synth.MoeConfig):
+def shape_of(cfg: synth.MoeConfig, capacity=None):
     from routing_permute_grouped_moe_amd.layer import LayerShape
     return LayerShape(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, k=cfg.k, dtype=torch_dtype(cfg),
-                      g0=cfg.g0, G=cfg.G, shared=cfg.shared, router=cfg.router)
+                      g0=cfg.g0, G=cfg.G, shared=cfg.shared, router=cfg.router,
+                      capacity=capacity)
 
 
 def make_layer(cfg: synth.MoeConfig, inp: synth.Inputs, overlap: bool = True,
-               recompute: bool = False):
+               recompute: bool = False, capacity=None):
     from routing_permute_grouped_moe_amd.layer import MoeLayer
-    L = MoeLayer(shape_of(cfg), overlap=overlap, recompute=recompute)
+    L = MoeLayer(shape_of(cfg, capacity), overlap=overlap, recompute=recompute)
     dt = torch_dtype(cfg)
     L.x.copy_(dev(inp.x, dt))
     L.dy.copy_(dev(inp.dy, dt))

@@ -76,9 +76,9 @@ def test_route_rejects_null_and_negative(abi):
 def test_zero_tokens_is_a_noop(abi):
     assert status(abi, "moe_route", None, 0, 8, 2, None, None, None) == abi.MOE_OK
     assert status(abi, "moe_route_bwd", None, None, None, 0, 8, 2, None, None) == abi.MOE_OK
-    assert status(abi, "moe_unpermute_combine", None, None, None, None, 1, 0, 128, 2, None,
+    assert status(abi, "moe_unpermute_combine", None, None, None, None, 1, 0, 128, 2, 0, None,
                   None) == abi.MOE_OK
-    assert status(abi, "moe_permute_bwd", None, None, 1, 0, 128, 2, None, None, None,
+    assert status(abi, "moe_permute_bwd", None, None, 1, 0, 128, 2, 0, None, None, None,
                   None) == abi.MOE_OK
 
 
@@ -92,13 +92,16 @@ def test_permute_workspace(abi):
 
 def test_shape_limits(abi):
     # H not a multiple of 64
-    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 1, 4, 100, 2, FAKE, None)
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 1, 4, 100, 2, 8, FAKE,
+                None)
     assert st == abi.MOE_ERR_UNSUPPORTED
     # misaligned pointer
-    st = status(abi, "moe_unpermute_combine", FAKE_ODD, FAKE, FAKE, None, 1, 4, 128, 2, FAKE, None)
+    st = status(abi, "moe_unpermute_combine", FAKE_ODD, FAKE, FAKE, None, 1, 4, 128, 2, 8, FAKE,
+                None)
     assert st == abi.MOE_ERR_INVALID_ARG
     # unknown dtype
-    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 7, 4, 128, 2, FAKE, None)
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 7, 4, 128, 2, 8, FAKE,
+                None)
     assert st == abi.MOE_ERR_INVALID_ARG
     # grouped GEMM: I not a multiple of 64, window beyond 1024 experts
     st = status(abi, "moe_grouped_gemm_fwd", FAKE, FAKE, 0, 8, 64, 1, 128, 96, FAKE, FAKE, FAKE,
@@ -112,7 +115,8 @@ def test_shape_limits(abi):
     assert st2 == abi.MOE_ERR_WORKSPACE
     assert st == abi.MOE_ERR_UNSUPPORTED
     # a row longer than the row kernels keep in registers
-    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 0, 4, 16384, 2, FAKE, None)
+    st = status(abi, "moe_unpermute_combine", FAKE, FAKE, FAKE, None, 0, 4, 16384, 2, 8, FAKE,
+                None)
     assert st == abi.MOE_ERR_UNSUPPORTED
 
 

@@ -141,13 +141,13 @@ def test_combine_and_backward(abi, T, E, k, H, dt):
     tol = TOL[dt]
     for with_shared in (False, True):
         y = torch.empty(T, H, dtype=tdt, device="cuda")
-        abi.moe_unpermute_combine(YP, RM, G, YS if with_shared else None, code, T, H, k, y)
+        abi.moe_unpermute_combine(YP, RM, G, YS if with_shared else None, code, T, H, k, T * k, y)
         torch.cuda.synchronize()
         ref = oracle.combine(yp, rmap, gate, ys if with_shared else None)
         assert rel_err(host(y), ref) <= tol
     dyp = torch.empty(R, H, dtype=tdt, device="cuda")
     dgate = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    abi.moe_unpermute_combine_bwd(DY, YP, RM, G, code, T, H, k, dyp, dgate)
+    abi.moe_unpermute_combine_bwd(DY, YP, RM, G, code, T, H, k, T * k, dyp, dgate)
     torch.cuda.synchronize()
     rdyp, rdg = oracle.combine_backward(dy, yp, rmap, gate)
     assert rel_err(host(dyp), rdyp) <= tol
@@ -157,11 +157,11 @@ def test_combine_and_backward(abi, T, E, k, H, dt):
     a0 = _store(r.standard_normal((T, H)), dt)
     a1 = _store(r.standard_normal((T, H)), dt)
     dx = torch.empty(T, H, dtype=tdt, device="cuda")
-    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, dev(a0, tdt), dev(a1, tdt), dx)
+    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, T * k, dev(a0, tdt), dev(a1, tdt), dx)
     torch.cuda.synchronize()
     ref = oracle.permute_backward(dxp, rmap) + a0 + a1
     assert rel_err(host(dx), ref) <= tol
-    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, None, None, dx)
+    abi.moe_permute_bwd(dev(dxp, tdt), RM, code, T, H, k, T * k, None, None, dx)
     torch.cuda.synchronize()
     assert rel_err(host(dx), oracle.permute_backward(dxp, rmap)) <= tol
 
