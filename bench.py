@@ -145,14 +145,20 @@ def measured_traffic(call):
         return None
 
 
-def recompute_variant(L, steps, warmup):
-    """Time the same step with the recompute variant (no saved xp / act) on
-    the same parameters and inputs; report the activation bytes each path
-    keeps from the forward for the backward."""
+def variant(L, steps, warmup, recompute=False, capacity=None):
+    """Time the same step in a variant of the layer on the same parameters
+    and inputs: the recompute variant (no saved xp / act; reports the
+    activation bytes each path keeps from the forward for the backward) or
+    drop-and-pad with ``capacity`` rows per expert (reports the pairs
+    dropped)."""
+    import dataclasses
+
+    import numpy as np
     import torch
 
     from routing_permute_grouped_moe_amd.layer import MoeLayer
-    B = MoeLayer(L.s, overlap=L.overlap, recompute=True)
+    shape = dataclasses.replace(L.s, capacity=capacity)
+    B = MoeLayer(shape, overlap=L.overlap, recompute=recompute)
     for n in ("x", "dy", "w13", "w2", "wg", "logits", "ws13", "ws2"):
         if getattr(L, n) is not None:
             getattr(B, n).copy_(getattr(L, n))
@@ -181,9 +187,18 @@ def recompute_variant(L, steps, warmup):
         for i, c in enumerate(calls)}
     out = {"ms_per_step": round(wall * 1e3 / steps, 4),
            "tokens_per_s": round(L.s.T * steps / wall, 1),
-           "activation_bytes_kept": B.saved_bytes(),
-           "saving_path_activation_bytes_kept": L.saved_bytes(),
            "ms_per_call": per_call}
+    if recompute:
+        out["activation_bytes_kept"] = B.saved_bytes()
+        out["saving_path_activation_bytes_kept"] = L.saved_bytes()
+    if capacity is not None:
+        counts = B.counts.cpu().numpy().astype(np.int64)
+        g0, G = L.s.g0, L.s.groups
+        out.update(capacity_rows_per_expert=capacity,
+                   dropped_pairs=int(np.maximum(counts - capacity, 0).sum()),
+                   pairs=int(counts.sum()),
+                   gemm_rows_local=G * capacity,
+                   gemm_rows_local_dropless=int(counts[g0:g0 + G].sum()))
     del B
     torch.cuda.empty_cache()
     return out
@@ -294,7 +309,11 @@ def main():
         "phases": phases,
     }
     if not args.no_variants and cfg.dtype == "bf16":
-        out["variants"] = {"recompute": recompute_variant(L, args.steps, args.warmup)}
+        import math
+        C = math.ceil(1.2 * cfg.T * cfg.k / cfg.E)   # capacity factor 1.2
+        out["variants"] = {
+            "recompute": variant(L, args.steps, args.warmup, recompute=True),
+            "drop_and_pad_cf1.2": variant(L, args.steps, args.warmup, capacity=C)}
     del L
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
