@@ -91,6 +91,12 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
+// Streaming write (cache policy nt): measured 3-6% faster for the gathers'
+// row outputs (combine, its backward, the permute backward); the permute's
+// k-fold row scatter is faster with plain stores.
+__device__ __forceinline__ void buf_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
+}
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

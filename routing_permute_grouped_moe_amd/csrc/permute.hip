@@ -371,7 +371,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[u][i] += tmp[i];
       }
-      if (q < nchunk) buf_store16(out, (uint32_t)q * 16u, pack16(acc[u], T()));
+      if (q < nchunk) buf_store16_nt(out, (uint32_t)q * 16u, pack16(acc[u], T()));
     }
   }
 }
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
 #pragma unroll
     for (int u = 0; u < ROW_QB; ++u) {
       const int q = q0 + u * ROW_THREADS;
-      if (q < nchunk) buf_store16(out, (uint32_t)q * 16u, pack16(acc[u], T()));
+      if (q < nchunk) buf_store16_nt(out, (uint32_t)q * 16u, pack16(acc[u], T()));
     }
   }
 }
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
               part[jj] += d[i] * tmp[i];
               o[i] = g * d[i];
             }
-            if (q < nchunk) buf_store16(dst, rb + (uint32_t)q * 16u, pack16(o, T()));
+            if (q < nchunk) buf_store16_nt(dst, rb + (uint32_t)q * 16u, pack16(o, T()));
           }
         }
     }

@@ -90,7 +90,10 @@ def test_route_deterministic(abi):
 
 PERM_CASES = [(1, 8, 2, 128, "f32"), (31, 8, 2, 128, "f32"), (33, 16, 4, 256, "bf16"),
               (1000, 64, 6, 2048, "bf16"), (513, 256, 8, 7680, "bf16"), (40, 5, 5, 64, "f32"),
-              (2048, 1024, 16, 128, "bf16"), (100, 3, 1, 8192, "f32")]
+              (2048, 1024, 16, 128, "bf16"), (100, 3, 1, 8192, "f32"),
+              # maximum sizes: every token picks all 1024 experts; bf16 rows
+              # at the 32 KB a row kernel keeps in registers
+              (8, 1024, 1024, 64, "bf16"), (77, 16, 4, 16384, "bf16")]
 
 
 def _perm_inputs(T, E, k, H, dt, seed):
@@ -222,6 +225,9 @@ GMM_CASES = [
     # per-XCD counters hand out many tiles
     ([int(c) for c in np.random.default_rng(7).integers(0, 60, 150)], 1024, 512, 0, None, 40,
      "bf16"),
+    # the largest window: 1024 experts, most of them empty or tiny
+    ([int(c) for c in np.random.default_rng(9).integers(0, 4, 1024) * (
+        np.random.default_rng(10).random(1024) < 0.3)], 128, 64, 0, None, 0, "bf16"),
 ]
 
 
