@@ -230,7 +230,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
 #pragma unroll
       for (int i = 0; i < ROW_MAXC; ++i) {
         int q = q0 + i * ROW_THREADS + threadIdx.x;
-        if (q < nchunk) buf_store16(dst, rb + (uint32_t)q * 16u, v[i]);
+        if (q < nchunk) buf_store16_nt(dst, rb + (uint32_t)q * 16u, v[i]);
       }
     }
   }
