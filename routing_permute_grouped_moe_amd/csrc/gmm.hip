@@ -835,12 +835,15 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     };
 
     // 8 values at element elem of an output (dropped unless ok)
+    // every output leaves with the streaming cache policy: measured ~1.5%
+    // faster over the layer step than plain stores (also with yp or act kept
+    // cached for the kernel that reads them next)
     auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, const float* v) {
       if constexpr (sizeof(T) == 2) {
-        buf_store16(rs, ok ? elem * 2u : DROP, pack16(v, T()));
+        buf_store16_nt(rs, ok ? elem * 2u : DROP, pack16(v, T()));
       } else {
-        buf_store16(rs, ok ? elem * 4u : DROP, pack16(v, T()));
-        buf_store16(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
+        buf_store16_nt(rs, ok ? elem * 4u : DROP, pack16(v, T()));
+        buf_store16_nt(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
       }
     };
     // 8 values at element elem of an operand (zeros unless ok)
@@ -1001,8 +1004,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
             emit(hc, [&](int row, int c, const float* v) {
               bool ok;
               const uint32_t e = place(row, c, ok);
-              buf_store16(cr, ok ? e * 4u : DROP, pack16(v, 0.0f));
-              buf_store16(cr, ok ? e * 4u + 16u : DROP, pack16(v + 4, 0.0f));
+              buf_store16_nt(cr, ok ? e * 4u : DROP, pack16(v, 0.0f));
+              buf_store16_nt(cr, ok ? e * 4u + 16u : DROP, pack16(v + 4, 0.0f));
             });
           } else {
             emit(hc, [&](int row, int c, const float* v) {
