@@ -200,8 +200,8 @@ __device__ __forceinline__ long long pair_row(const int32_t* __restrict__ idx,
 template <int ESZ>
 __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ hist, int T, int H, int E,
-    int k, int cap, long long R, void* __restrict__ xp, int32_t* __restrict__ row_id_map,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ hist, int H, int E, int k,
+    int cap, long long R, void* __restrict__ xp, int32_t* __restrict__ row_id_map,
     int32_t* __restrict__ src_token) {
   __shared__ uint32_t rofs[MOE_MAX_E];
   const int t = blockIdx.x;
@@ -310,8 +310,8 @@ __device__ __forceinline__ u32x4 row_chunk(const __amdgpu_buffer_rsrc_t& rs, uin
 
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
-    const T* __restrict__ dxp, const int32_t* __restrict__ row_id_map, int Tn, int H, int k,
-    long long R, const T* __restrict__ add0, const T* __restrict__ add1, T* __restrict__ dx) {
+    const T* __restrict__ dxp, const int32_t* __restrict__ row_id_map, int H, int k, long long R,
+    const T* __restrict__ add0, const T* __restrict__ add1, T* __restrict__ dx) {
   constexpr int VEC = Elem<T>::VEC;
   __shared__ uint32_t rofs[MOE_MAX_E];
   const int t = blockIdx.x;
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_bwd_kernel(
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
     const T* __restrict__ yp, const int32_t* __restrict__ row_id_map,
-    const float* __restrict__ gate, const T* __restrict__ ys, int Tn, int H, int k, long long R,
+    const float* __restrict__ gate, const T* __restrict__ ys, int H, int k, long long R,
     T* __restrict__ y) {
   constexpr int VEC = Elem<T>::VEC;
   __shared__ uint32_t rofs[MOE_MAX_E];
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ yp, const int32_t* __restrict__ row_id_map,
-    const float* __restrict__ gate, int Tn, int H, int k, long long R, T* __restrict__ dyp,
+    const float* __restrict__ gate, int H, int k, long long R, T* __restrict__ dyp,
     float* __restrict__ dgate) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int NW = ROW_THREADS / MOE_WAVE;
@@ -608,10 +608,10 @@ static int permute_impl(const char* fn, const void* x, int dt, const int32_t* id
                          idx, offsets, hist, T, E, k, cap, R, row_id_map, src_token);
     } else if (dt == MOE_BF16) {
       hipLaunchKernelGGL(permute_scatter_kernel<2>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
-                         offsets, hist, T, H, E, k, cap, R, xp, row_id_map, src_token);
+                         offsets, hist, H, E, k, cap, R, xp, row_id_map, src_token);
     } else {
       hipLaunchKernelGGL(permute_scatter_kernel<4>, dim3(T), dim3(ROW_THREADS), 0, s, x, idx,
-                         offsets, hist, T, H, E, k, cap, R, xp, row_id_map, src_token);
+                         offsets, hist, H, E, k, cap, R, xp, row_id_map, src_token);
     }
     MOE_TRY(moe_check_launch(fn));
   }
@@ -693,11 +693,11 @@ extern "C" int moe_permute_bwd(const void* dxp, const int32_t* row_id_map, int d
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const bf16_t*)dxp, row_id_map, T, H, k, (long long)R, (const bf16_t*)add0,
+                       (const bf16_t*)dxp, row_id_map, H, k, (long long)R, (const bf16_t*)add0,
                        (const bf16_t*)add1, (bf16_t*)dx);
   else
     hipLaunchKernelGGL(permute_bwd_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const float*)dxp, row_id_map, T, H, k, (long long)R, (const float*)add0,
+                       (const float*)dxp, row_id_map, H, k, (long long)R, (const float*)add0,
                        (const float*)add1, (float*)dx);
   return moe_check_launch(fn);
 }
@@ -717,11 +717,11 @@ extern "C" int moe_unpermute_combine(const void* yp, const int32_t* row_id_map, 
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const bf16_t*)yp, row_id_map, gate, (const bf16_t*)y_shared, T, H, k,
+                       (const bf16_t*)yp, row_id_map, gate, (const bf16_t*)y_shared, H, k,
                        (long long)R, (bf16_t*)y);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s, (const float*)yp,
-                       row_id_map, gate, (const float*)y_shared, T, H, k, (long long)R,
+                       row_id_map, gate, (const float*)y_shared, H, k, (long long)R,
                        (float*)y);
   return moe_check_launch(fn);
 }
@@ -742,11 +742,11 @@ extern "C" int moe_unpermute_combine_bwd(const void* dy, const void* yp, const i
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const bf16_t*)dy, (const bf16_t*)yp, row_id_map, gate, T, H, k,
+                       (const bf16_t*)dy, (const bf16_t*)yp, row_id_map, gate, H, k,
                        (long long)R, (bf16_t*)dyp, dgate);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(ROW_THREADS), 0, s,
-                       (const float*)dy, (const float*)yp, row_id_map, gate, T, H, k,
+                       (const float*)dy, (const float*)yp, row_id_map, gate, H, k,
                        (long long)R, (float*)dyp, dgate);
   return moe_check_launch(fn);
 }
