@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
   }
 }
 
-// dbias: per-chunk column sums (256 tokens per chunk), then a fixed-order sum.
+// dbias: per-chunk column sums (COLSUM_ROWS tokens per chunk), then a fixed-order sum.
 #define COLSUM_ROWS 64   // rows of one column partial sum
 __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ dl, int T,
                                                           int E, float* __restrict__ part) {
@@ -216,21 +216,30 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restric
   for (int i = 0; i < COLSUM_ROWS; ++i) s += v[i];
   part[(long long)c * E + e] = s;
 }
+// out[e] = sum of the partials of column e, in fp64: a block holds 64
+// columns x 4 slices of the chunks; each slice adds its chunks in order
+// (requested 16 at a time), then the 4 slice sums are added in slice order.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part,
                                                            int nchunk, int E,
                                                            float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
-  // partials requested 32 at a time, then added in chunk order (fp64)
+  __shared__ double red[4][64];
+  const int col = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + col;
+  const int per = (nchunk + 3) / 4;
+  const int c0 = sl * per, c1 = min(nchunk, c0 + per);
   double s = 0.0;
-  for (int c0 = 0; c0 < nchunk; c0 += 32) {
-    float v[32];
+  if (e < E) {
+    for (int cb = c0; cb < c1; cb += 16) {
+      float v[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = c0 + i < nchunk ? part[(long long)(c0 + i) * E + e] : 0.f;
+      for (int i = 0; i < 16; ++i) v[i] = cb + i < c1 ? part[(long long)(cb + i) * E + e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) s += (double)v[i];
+      for (int i = 0; i < 16; ++i) s += (double)v[i];
+    }
   }
-  out[e] = (float)s;
+  red[sl][col] = s;
+  __syncthreads();
+  if (sl == 0 && e < E) out[e] = (float)(((red[0][col] + red[1][col]) + red[2][col]) + red[3][col]);
 }
 
 static int grid_for(long long n) {
@@ -325,7 +334,7 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
                        dim3(256), 0, s, (const float*)nullptr, 0LL, 0LL, (const float*)nullptr, 0LL,
                        0LL, (const float*)nullptr, H, E, 0, dwg, (long long)E);
     if (dbias)
-      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 255) / 256), dim3(256), 0, s,
+      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 63) / 64), dim3(256), 0, s,
                          (const float*)nullptr, 0, E, dbias);
     return moe_check_launch(fn);
   }
@@ -367,7 +376,7 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
       float* colpart = (float*)(w + L.colpart);
       hipLaunchKernelGGL(colsum_part_kernel, dim3(nchunk, (E + 255) / 256), dim3(256), 0, s,
                          dlogits, T, E, colpart);
-      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 255) / 256), dim3(256), 0, s,
+      hipLaunchKernelGGL(colsum_final_kernel, dim3((E + 63) / 64), dim3(256), 0, s,
                          (const float*)colpart, nchunk, E, dbias);
       MOE_TRY(moe_check_launch(fn));
     }
