@@ -44,7 +44,9 @@ def _store(a, dt):
 
 ROUTE_CASES = [(64, 8, 2, "normal"), (300, 64, 6, "normal"), (257, 256, 8, "ties"),
                (100, 1024, 8, "normal"), (33, 1024, 1024, "normal"), (50, 1, 1, "normal"),
-               (70, 5, 5, "ties"), (129, 200, 3, "ties")]
+               (70, 5, 5, "ties"), (129, 200, 3, "ties"),
+               # every per-lane width of the kernels: E = 100 (2), E = 400 (8)
+               (90, 100, 4, "ties"), (77, 400, 8, "normal")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
