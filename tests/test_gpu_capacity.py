@@ -180,3 +180,24 @@ def test_capacity_holding_every_pair_equals_dropless():
     torch.cuda.synchronize()
     for n in ("y", "dx", "dw13", "dw2", "dgate", "dlogits", "dwg"):
         assert torch.equal(getattr(A, n), getattr(B, n)), n
+
+
+def test_recompute_with_capacity_equals_saving_capacity():
+    """Recompute on drop-and-pad: unfilled rows (src_token -1) gather zeros,
+    so the results equal the saving drop-and-pad layer bit for bit."""
+    cfg = synth.get_config("pangu", T=1024)
+    C = oracle.capacity(cfg.T, cfg.k, cfg.E, 1.2)
+    inp = synth.make_inputs(cfg)
+    A = make_layer(cfg, inp, capacity=C)
+    B = make_layer(cfg, inp, capacity=C, recompute=True)
+    A.forward()
+    B.forward()
+    torch.cuda.synchronize()
+    B.act.fill_(float("nan"))
+    B.sh_act.fill_(float("nan"))
+    A.backward()
+    B.backward()
+    torch.cuda.synchronize()
+    assert (host(A.row_id_map) < 0).any()
+    for n in ("y", "dx", "dw13", "dw2", "dgate", "dws13", "dws2", "dwg"):
+        assert torch.equal(getattr(A, n), getattr(B, n)), n
