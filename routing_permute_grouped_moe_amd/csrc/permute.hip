@@ -3,22 +3,32 @@
 // Fig. 3; [MoE-ops] Host-Device section, Fig. 4: the per-expert counts are
 // produced and consumed on the device, never read back by the host).
 //
-// Stable rank without atomics: tokens are cut into chunks of PERM_CHUNK; one
-// wavefront per chunk walks its tokens in order and counts, per expert, the
-// earlier tokens of the chunk (the local rank).  A column scan over chunks
-// gives each chunk's base inside every expert group and the counts; a scan
-// over experts gives the group offsets.  The row of pair (t,j) is then
-// offsets[e] + chunk base + local rank, unique and in token order.
+// Stable rank without atomics: the T*k (token, slot) pairs, in pair order,
+// are cut into blocks of RANK_BLOCK_PAIRS.  Inside a block every wavefront
+// ranks 64 pairs at a time: the lanes holding the same expert find each other
+// with one ballot per bit of the expert id, so a pair's rank among the step's
+// pairs of its expert is the number of lower lanes that match, and the
+// wave's per-expert counter in LDS gives the earlier steps' pairs.  The
+// waves' counters are then scanned in wave order, which makes the rank
+// relative to the block.  One more workgroup scans the blocks' counts per
+// expert (each block's base inside every expert group, and the counts) and
+// the counts over experts (the group offsets).  The row of pair (t,j) is
+// offsets[e] + block base + rank in the block: unique and in token order.
 //
 // The row moves are token-centric: one workgroup per token reads the token's
 // row once with 16-byte lanes and writes (or gathers) its k rows.
 #include "validate.hpp"
 
-#define PERM_CHUNK 32      // tokens per rank chunk
+#define RANK_WAVES 16      // wavefronts of a rank workgroup
+#define RANK_STEPS 4       // 64-pair steps per wavefront
+#define RANK_WAVE_PAIRS (MOE_WAVE * RANK_STEPS)
+#define RANK_BLOCK_PAIRS (RANK_WAVES * RANK_WAVE_PAIRS)   // 4096 pairs per block
 #define ROW_THREADS 256    // threads of a row-moving workgroup
 #define ROW_MAXC 8         // 16-byte chunks per thread kept in registers
 
-static inline long long perm_chunks(int T) { return (T + PERM_CHUNK - 1) / PERM_CHUNK; }
+static inline long long rank_blocks(int T, int k) {
+  return ((long long)T * k + RANK_BLOCK_PAIRS - 1) / RANK_BLOCK_PAIRS;
+}
 
 // Byte offset of a row that is not there (a dropped pair, or a row index
 // outside [0, R)): every permuted-row buffer's descriptor stops at or before
@@ -34,99 +44,105 @@ __host__ __device__ __forceinline__ uint32_t rows_bytes(long long R, uint32_t ro
 
 // ---------------------------------------------------------------- rank
 
-__global__ __launch_bounds__(MOE_WAVE) void permute_rank_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int32_t* __restrict__ local_rank,
-    int32_t* __restrict__ hist) {
-  __shared__ int cnt[MOE_MAX_E];
-  __shared__ int ids[PERM_CHUNK * 64];
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x;
-  const int t0 = c * PERM_CHUNK;
-  const int nt = min(PERM_CHUNK, T - t0);
-  for (int e = lane; e < E; e += MOE_WAVE) cnt[e] = 0;
-  // stage the chunk's expert ids (nt*k of them) through LDS in pieces of
-  // PERM_CHUNK*64 values
-  const long long base = (long long)t0 * k;
-  const int total = nt * k;
-  const int piece = ((PERM_CHUNK * 64) / k) * k;  // whole tokens per piece (k <= 1024)
-  for (int p0 = 0; p0 < total; p0 += piece) {
-    const int pn = min(piece, total - p0);
-    for (int i = lane; i < pn; i += MOE_WAVE) {
-      int e = idx[base + p0 + i];
-      ids[i] = (e >= 0 && e < E) ? e : 0;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // walk the pairs in order; the k experts of one token are distinct, so
-    // the lanes of one step touch distinct counters
-    for (int q = 0; q < pn; q += k) {
-      for (int j = lane; j < k && q + j < pn; j += MOE_WAVE) {
-        int e = ids[q + j];
-        int r = cnt[e];
-        cnt[e] = r + 1;
-        local_rank[base + p0 + q + j] = r;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
+// local_rank[p] <- rank of pair p among the pairs of its expert in its block
+// (pair order); hist[b][e] <- pairs of expert e in block b.  Dynamic LDS:
+// RANK_WAVES * E counters.  ebits = bits of the largest expert id.
+__global__ __launch_bounds__(MOE_WAVE * RANK_WAVES) void permute_rank_kernel(
+    const int32_t* __restrict__ idx, long long P, int E, int ebits,
+    int32_t* __restrict__ local_rank, int32_t* __restrict__ hist) {
+  extern __shared__ int wcnt[];   // [RANK_WAVES][E]
+  const int lane = threadIdx.x % MOE_WAVE, wave = threadIdx.x / MOE_WAVE;
+  for (int i = threadIdx.x; i < RANK_WAVES * E; i += MOE_WAVE * RANK_WAVES) wcnt[i] = 0;
+  const long long p0 = (long long)blockIdx.x * RANK_BLOCK_PAIRS + wave * RANK_WAVE_PAIRS + lane;
+  int ev[RANK_STEPS], rv[RANK_STEPS];
+#pragma unroll
+  for (int s = 0; s < RANK_STEPS; ++s) {
+    const long long p = p0 + s * MOE_WAVE;
+    int e = p < P ? idx[p] : -1;
+    ev[s] = p < P ? ((e >= 0 && e < E) ? e : 0) : -1;
   }
-  for (int e = lane; e < E; e += MOE_WAVE) hist[(long long)c * E + e] = cnt[e];
-}
-
-// Column scan over chunks: hist[c][e] <- sum_{c' < c} hist[c'][e];
-// counts[e] <- sum_c hist[c][e].  Block: 64 experts x 16 chunk slices.
-#define SCAN_SLICES 16
-__global__ __launch_bounds__(MOE_WAVE * SCAN_SLICES) void permute_colscan_kernel(
-    int32_t* __restrict__ hist, int nchunks, int E, int32_t* __restrict__ counts) {
-  __shared__ int part[SCAN_SLICES][MOE_WAVE];
-  const int lane = threadIdx.x % MOE_WAVE;
-  const int s = threadIdx.x / MOE_WAVE;
-  const int e = blockIdx.x * MOE_WAVE + lane;
-  const int per = (nchunks + SCAN_SLICES - 1) / SCAN_SLICES;
-  const int c0 = s * per, c1 = min(nchunks, c0 + per);
-  int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) sum += hist[(long long)c * E + e];
-  part[s][lane] = sum;
   __syncthreads();
-  int run = 0;
-  for (int i = 0; i < s; ++i) run += part[i][lane];
-  if (e < E) {
-    for (int c = c0; c < c1; ++c) {
-      long long o = (long long)c * E + e;
-      int v = hist[o];
-      hist[o] = run;
+  int* cnt = wcnt + wave * E;
+  const unsigned long long below_me = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int s = 0; s < RANK_STEPS; ++s) {
+    const bool valid = ev[s] >= 0;
+    const int e = valid ? ev[s] : 0;
+    // lanes with the same expert id: agree on every bit
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int below = __popcll(m & below_me);
+    const int n = __popcll(m);
+    // every lane reads the counter before the lowest matching lane writes
+    // it (one wavefront's LDS instructions execute in order)
+    const int base = valid ? cnt[e] : 0;
+    if (valid && below == 0) cnt[e] = base + n;
+    rv[s] = base + below;
+  }
+  __syncthreads();
+  // the waves' counts of each expert -> exclusive prefix in wave order
+  for (int e = threadIdx.x; e < E; e += MOE_WAVE * RANK_WAVES) {
+    int run = 0;
+    for (int w = 0; w < RANK_WAVES; ++w) {
+      const int v = wcnt[w * E + e];
+      wcnt[w * E + e] = run;
       run += v;
     }
-    if (s == SCAN_SLICES - 1) counts[e] = run;
+    hist[(long long)blockIdx.x * E + e] = run;
   }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < RANK_STEPS; ++s)
+    if (ev[s] >= 0) local_rank[p0 + s * MOE_WAVE] = cnt[ev[s]] + rv[s];
 }
 
-// offsets = exclusive scan of counts, offsets[E] = total.  One block of 1024.
-__global__ __launch_bounds__(1024) void permute_offsets_kernel(const int32_t* __restrict__ counts,
-                                                               int E, int32_t* __restrict__ offsets) {
+// One workgroup of 1024: hist[b][e] <- sum_{b' < b} hist[b'][e] (the block's
+// base inside group e); counts[e] <- sum_b hist[b][e]; offsets = exclusive
+// scan of counts (dropless, cap < 0) or e * cap (drop-and-pad), and
+// offsets[E] the end.  Thread i scans slice i / E of expert i % E's blocks.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ hist, int nblk,
+                                                            int E, int cap,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int part[1024];
   __shared__ int buf[1024];
   const int i = threadIdx.x;
-  int v = i < E ? counts[i] : 0;
-  buf[i] = v;
+  const int S = 1024 / E;   // slices per expert (E <= 1024)
+  const int e = i % E, s = i / E;
+  const bool on = s < S;
+  const int per = (nblk + S - 1) / S;
+  const int b0 = on ? s * per : 0, b1 = on ? min(nblk, b0 + per) : 0;
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += hist[(long long)b * E + e];
+  part[i] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < s && on; ++q) run += part[q * E + e];
+  for (int b = b0; b < b1; ++b) {
+    const long long o = (long long)b * E + e;
+    const int v = hist[o];
+    hist[o] = run;
+    run += v;
+  }
+  int tot = 0;
+  if (i < E) {
+    for (int q = 0; q < S; ++q) tot += part[q * E + i];
+    counts[i] = tot;
+  }
+  buf[i] = tot;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    int add = i >= o ? buf[i - o] : 0;
+    const int add = i >= o ? buf[i - o] : 0;
     __syncthreads();
     buf[i] += add;
     __syncthreads();
   }
-  if (i < E) offsets[i] = buf[i] - v;
-  if (i == E - 1) offsets[E] = buf[i];
-}
-
-__global__ __launch_bounds__(1024) void permute_zero_kernel(int32_t* counts, int32_t* offsets,
-                                                            int E) {
-  for (int i = threadIdx.x; i <= E; i += 1024) {
-    if (i < E) counts[i] = 0;
-    offsets[i] = 0;
-  }
+  if (i < E) offsets[i] = cap < 0 ? buf[i] - tot : i * cap;
+  if (i == E - 1) offsets[E] = cap < 0 ? buf[i] : E * cap;
 }
 
 // ---------------------------------------------------------------- load statistics
@@ -180,18 +196,20 @@ __global__ __launch_bounds__(1024) void load_stats_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------- scatter
 
-// Row of pair p = (t, j) of chunk c: its stable rank inside expert e is the
-// chunk's base plus the local rank (held in row_id_map until now).  Dropless
-// (cap < 0): row = offsets[e] + rank.  Drop-and-pad (cap >= 0, offsets[e] =
-// e * cap): the pair keeps that row if rank < cap, else it is dropped (-1).
+// Row of pair p = (t, j): its stable rank inside expert e is the base of
+// p's rank block in group e plus the rank in the block (held in row_id_map
+// until now).  Dropless (cap < 0): row = offsets[e] + rank.  Drop-and-pad
+// (cap >= 0, offsets[e] = e * cap): the pair keeps that row if rank < cap,
+// else it is dropped (-1).
 __device__ __forceinline__ long long pair_row(const int32_t* __restrict__ idx,
                                               const int32_t* __restrict__ offsets,
                                               const int32_t* __restrict__ hist,
                                               const int32_t* __restrict__ row_id_map, long long p,
-                                              int c, int E, int cap, long long R) {
+                                              int E, int cap, long long R) {
   int e = idx[p];
   e = (e >= 0 && e < E) ? e : 0;
-  const long long rank = (long long)hist[(long long)c * E + e] + row_id_map[p];
+  const long long b = p / RANK_BLOCK_PAIRS;
+  const long long rank = (long long)hist[b * E + e] + row_id_map[p];
   if (cap >= 0 && rank >= cap) return -1;
   long long row = (long long)offsets[e] + rank;
   return row < 0 ? 0 : (row >= R ? R - 1 : row);
@@ -205,11 +223,10 @@ __global__ __launch_bounds__(ROW_THREADS) void permute_scatter_kernel(
     int32_t* __restrict__ src_token) {
   __shared__ uint32_t rofs[MOE_MAX_E];
   const int t = blockIdx.x;
-  const int c = t / PERM_CHUNK;
   const uint32_t row_bytes = (uint32_t)H * ESZ;
   for (int j = threadIdx.x; j < k; j += ROW_THREADS) {
     const long long p = (long long)t * k + j;
-    const long long row = pair_row(idx, offsets, hist, row_id_map, p, c, E, cap, R);
+    const long long row = pair_row(idx, offsets, hist, row_id_map, p, E, cap, R);
     row_id_map[p] = (int)row;
     if (row >= 0) src_token[row] = t;
     rofs[j] = row_off(row, R, row_bytes);
@@ -244,15 +261,9 @@ __global__ __launch_bounds__(256) void permute_maps_kernel(
   const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
   if (p >= (long long)T * k) return;
   const int t = (int)(p / k);
-  const long long row = pair_row(idx, offsets, hist, row_id_map, p, t / PERM_CHUNK, E, cap, R);
+  const long long row = pair_row(idx, offsets, hist, row_id_map, p, E, cap, R);
   row_id_map[p] = (int)row;
   if (row >= 0) src_token[row] = t;
-}
-
-// Drop-and-pad: offsets[e] = e * C (e = 0..E).
-__global__ __launch_bounds__(1024) void permute_cap_offsets_kernel(int32_t* __restrict__ offsets,
-                                                                   int E, int C) {
-  for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = e * C;
 }
 
 // Drop-and-pad: the rows [e*C + counts[e], (e+1)*C) that no pair fills get
@@ -554,7 +565,7 @@ static int perm_rows_check(const char* fn, int dt, long long R, int H) {
 extern "C" size_t moe_permute_workspace_bytes(int T, int E, int k) {
   (void)k;
   if (T <= 0 || E <= 0) return 0;
-  return (size_t)perm_chunks(T) * (size_t)E * sizeof(int32_t);
+  return (size_t)rank_blocks(T, k) * (size_t)E * sizeof(int32_t);
 }
 
 // Dropless (cap < 0, R = T*k) or drop-and-pad (cap = C >= 0, R = E*C).
@@ -581,25 +592,18 @@ static int permute_impl(const char* fn, const void* x, int dt, const int32_t* id
   if (R > 0) MOE_TRY(moe_need_ptr(src_token, fn, "src_token", 4));
   hipStream_t s = (hipStream_t)stream;
   int32_t* hist = (int32_t*)ws;
-  if (T == 0) {
-    // empty input: every group is empty (a fill kernel, not a memset node)
-    hipLaunchKernelGGL(permute_zero_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E);
-    MOE_TRY(moe_check_launch(fn));
-  } else {
-    const int nchunks = (int)perm_chunks(T);
-    hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(MOE_WAVE), 0, s, idx, T, E, k,
+  const int nblk = (int)rank_blocks(T, k);
+  if (T > 0) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nblk), dim3(MOE_WAVE * RANK_WAVES),
+                       (size_t)RANK_WAVES * E * sizeof(int), s, idx, (long long)T * k, E, ebits,
                        row_id_map, hist);
     MOE_TRY(moe_check_launch(fn));
-    hipLaunchKernelGGL(permute_colscan_kernel, dim3((E + MOE_WAVE - 1) / MOE_WAVE),
-                       dim3(MOE_WAVE * SCAN_SLICES), 0, s, hist, nchunks, E, counts);
-    MOE_TRY(moe_check_launch(fn));
   }
-  if (cap < 0) {
-    if (T > 0) hipLaunchKernelGGL(permute_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, E,
-                                  offsets);
-  } else {
-    hipLaunchKernelGGL(permute_cap_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, cap);
-  }
+  // (T = 0: no blocks, so every count is zero -- a fill kernel, not a memset node)
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nblk, E, cap, counts,
+                     offsets);
   MOE_TRY(moe_check_launch(fn));
   if (T > 0) {
     if (xp == nullptr) {

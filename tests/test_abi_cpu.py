@@ -84,7 +84,9 @@ def test_zero_tokens_is_a_noop(abi):
 
 def test_permute_workspace(abi):
     need = abi.moe_permute_workspace_bytes(100, 8, 2)
-    assert need >= 4 * 8 * ((100 + 31) // 32)
+    # one int per expert for every rank block of 4096 (token, slot) pairs
+    assert need == 4 * 8 * ((100 * 2 + 4095) // 4096)
+    assert abi.moe_permute_workspace_bytes(8192, 256, 8) == 4 * 256 * 16
     st = status(abi, "moe_permute", FAKE, 1, FAKE, 100, 128, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
                 FAKE, need - 4, None)
     assert st == abi.MOE_ERR_WORKSPACE

@@ -95,7 +95,9 @@ PERM_CASES = [(1, 8, 2, 128, "f32"), (31, 8, 2, 128, "f32"), (33, 16, 4, 256, "b
               (2048, 1024, 16, 128, "bf16"), (100, 3, 1, 8192, "f32"),
               # maximum sizes: every token picks all 1024 experts; bf16 rows
               # at the 32 KB a row kernel keeps in registers
-              (8, 1024, 1024, 64, "bf16"), (77, 16, 4, 16384, "bf16")]
+              (8, 1024, 1024, 64, "bf16"), (77, 16, 4, 16384, "bf16"),
+              # one expert; 32 rank blocks of 4096 pairs scanned in slices
+              (50, 1, 1, 64, "f32"), (16384, 256, 8, 64, "bf16")]
 
 
 def _perm_inputs(T, E, k, H, dt, seed):
