@@ -12,7 +12,9 @@ Backward: combine bwd -> grouped GEMM dX -> grouped GEMM dW -> route bwd ->
 
 With ``overlap`` (the default on a GPU) the work that does not depend on the
 routing runs on a second stream of the same priority: the shared expert's
-GEMMs (forward and backward) and the router backward.  The grouped GEMM draws
+GEMMs (forward: after the router projection, beside route, permute and the
+routed GEMMs; backward: beside everything up to the permute backward) and the
+router backward.  The grouped GEMM draws
 its tiles from per-XCD counters, so whichever kernel holds fewer CUs at the
 end of another one's last round simply takes fewer tiles; results are
 bitwise identical to the sequential order.
@@ -272,12 +274,15 @@ class MoeLayer:
         if self.overlap and s.shared:
             main, aux = self._streams(stream)
             ev_in, ev_sh = self._ev[0], self._ev[1]
+            # the router projection (a GEMM of its own) runs before the fork:
+            # beside the shared expert's GEMMs it only splits the CUs, while
+            # route and permute (latency and HBM bound) fill them in
+            if s.router:
+                self.router_fwd(main)
             ev_in.record(main)
             aux.wait_event(ev_in)
             self.gmm_fwd(aux, part="shared")            # needs x only
             ev_sh.record(aux)
-            if s.router:
-                self.router_fwd(main)
             self.route(main)
             self.permute(main)
             self.load_stats(main)
