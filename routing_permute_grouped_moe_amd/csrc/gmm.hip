@@ -490,25 +490,22 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   int* const ctr = a.cnt;   // [0, 8): per-XCD tile counters, [8]: finished workgroups
   const bool dyn = ctr != nullptr;
   int k = wix;              // index of this workgroup's tile inside the chunk
-  int grab = 0;             // thread 0: the counter value drawn during the last epilogue
+  int grab = 0;             // thread 0: the counter value drawn at the start of this tile
 
   for (bool first = true;; first = false) {
-    // every wave is done reading the ring (previous tile), the previous
-    // tile's stores have left, and the tile draw has returned
-    wait_vm<0>();
+    // every wave is done reading the ring (previous tile) and s_next holds
+    // the next tile; the previous tile's stores may still be draining --
+    // they overlap this tile's first copies (the copy waits below count them
+    // too, which only makes them wait longer)
     __syncthreads();
-    if (!first) {
-      if (dyn) {
-        if (tid == 0) s_next = wpx + grab;
-        __syncthreads();
-        k = s_next;
-      } else {
-        k += wpx;
-      }
-    }
+    if (!first) k = dyn ? s_next : k + wpx;
     k = uniform(k);
     const int tile_id = tile_of(k);
     if (tile_id >= total) break;
+    // draw the tile after this one now: the atomic returns long before its
+    // value is read, at the epilogue's full wait
+    if (dyn && tid == 0)
+      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // ---- locate the tile
     int g, m0, n0, rows0 = 0, rows = 0, kdim;
     if constexpr (MODE != DW) {
@@ -778,12 +775,9 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     int etid = threadIdx.x;
     asm volatile("" : "+v"(etid));
     const int elane = etid & 63;
-    wait_vm<0>();      // the empty copies past the last step have landed
+    wait_vm<0>();      // the empty copies past the last step (and the draw) have landed
+    if (dyn && tid == 0) s_next = wpx + grab;   // read after the next loop-top barrier
     __syncthreads();   // every wave is done with the ring
-    // draw the next tile now: the atomic's latency hides behind the epilogue
-    // (its value is read after the next iteration's full wait)
-    if (dyn && tid == 0)
-      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float* ep = (float*)smem;
     auto put = [&](auto fn0c, auto&& value) {
       // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
