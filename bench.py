@@ -58,24 +58,30 @@ CALLS = ["router_fwd", "route", "permute", "load_stats", "gmm_fwd", "combine", "
          "gmm_bwd_dw", "route_bwd", "router_bwd", "permute_bwd"]
 
 
-def algorithmic(cfg, rows_local):
-    """Algorithmic flops / bytes per call (routed rows only, no padding)."""
+def algorithmic(cfg, rows_local, active_local):
+    """Algorithmic flops / bytes per call (routed rows only, no padding).
+
+    An expert's weights are W13 [2I, H] and W2 [H, I]: 3 H I elements, read
+    once by the forward and by dX (experts that received rows), written once
+    as weight gradients by dW (every expert of the window, empty ones as
+    zeros)."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     b = 2 if cfg.dtype == "bf16" else 4
     rows = rows_local + (T if cfg.shared else 0)
     gmm_flops = 6.0 * rows * H * I
-    n_experts = cfg.groups + (1 if cfg.shared else 0)
-    gmm_w_bytes = n_experts * 6.0 * H * I * b
+    sh = 1 if cfg.shared else 0
+    w_read = (active_local + sh) * 3.0 * H * I * b
+    w_write = (cfg.groups + sh) * 3.0 * H * I * b
     out = {
         "router_fwd": {"flops": 2.0 * T * H * E, "bytes": T * H * b + H * E * 4 + T * E * 4},
         "route": {"bytes": 4.0 * T * E + 8.0 * T * k},
         "permute": {"bytes": (1 + k) * T * H * b + 12.0 * T * k},
         "load_stats": {"bytes": 8.0 * E + 8 + 4.0 * (E // (cfg.groups if E % cfg.groups == 0 else E))},
-        "gmm_fwd": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 3 * I) * b},
+        "gmm_fwd": {"flops": gmm_flops, "bytes": w_read + rows * (2 * H + 3 * I) * b},
         "combine": {"bytes": (k + 1) * T * H * b + 8.0 * T * k + (T * H * b if cfg.shared else 0)},
         "combine_bwd": {"bytes": T * H * b + 2.0 * T * k * H * b + 12.0 * T * k},
-        "gmm_bwd_dx": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 4 * I) * b},
-        "gmm_bwd_dw": {"flops": gmm_flops, "bytes": gmm_w_bytes + rows * (2 * H + 3 * I) * b},
+        "gmm_bwd_dx": {"flops": gmm_flops, "bytes": w_read + rows * (2 * H + 4 * I) * b},
+        "gmm_bwd_dw": {"flops": gmm_flops, "bytes": w_write + rows * (2 * H + 3 * I) * b},
         "route_bwd": {"bytes": 8.0 * T * E + 12.0 * T * k},
         "router_bwd": {"flops": 4.0 * T * H * E, "bytes": 2 * T * H * b + H * E * 4 + T * E * 4},
         "permute_bwd": {"bytes": (k + 1) * T * H * b + 4.0 * T * k
@@ -241,6 +247,7 @@ def main():
     torch.cuda.synchronize()
     rows = L.offsets.cpu().numpy()
     rows_local = int(rows[cfg.g0 + cfg.groups] - rows[cfg.g0])
+    active_local = int((L.counts.cpu().numpy()[cfg.g0:cfg.g0 + cfg.groups] > 0).sum())
 
     # timed region: K whole steps (the shared expert and the router backward on
     # a second stream unless --sequential), bracketed by device synchronisation
@@ -271,7 +278,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / wall
 
-    alg = algorithmic(cfg, rows_local)
+    alg = algorithmic(cfg, rows_local, active_local)
     phases = {}
     for c in calls:
         ms = per_call[c]
