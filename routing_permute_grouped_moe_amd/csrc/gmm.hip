@@ -699,122 +699,48 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         // halves measured ~10% fewer cycles per step than issuing them
         // together).  Steps past the end
         // copy through the empty descriptor, so every step looks the same.
-        if constexpr (MODE == DW) {
-          // (M is not a row count here; this loop is kept apart from the
-          // row-count builds below, which compile dW's loop measurably slower)
-          Frags<T, A_MN, B_MN> f0, f1;
-          f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
-          for (int kt = 0; kt < KT; ++kt) {
-            const char* cs = stage(kt);
-            const char* ns = stage(kt + 1);
+        Frags<T, A_MN, B_MN> f0, f1;
+        f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
+        for (int kt = 0; kt < KT; ++kt) {
+          const char* cs = stage(kt);
+          const char* ns = stage(kt + 1);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-                else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            // K step kt+1 has landed once at most the copies issued after it
-            // (step kt+2, and step kt+3's A copies) are outstanding; the
-            // barrier extends that to all waves and retires every read of the
-            // stage refilled next
-            // (GLOOP: also step kt+3's indices, issued right after step
-            // kt+1's B copies, and one index copy more per step since)
-            wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
-            __syncthreads();
-            u32x4 ivn;
-            if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-                else if (q - (FM + FN) < DMA_PER_OP) {
-                  if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
-                  else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-                } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
-                  issue_idx(kt + STAGES + 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-          }
-        } else {
-          // Built per count FA of this wave's A fragments that hold rows of the
-          // tile: in a tile of a group with few rows the upper fragments (and
-          // the lower waves) see padding only, so their MFMAs and A-fragment
-          // reads are left out (their accumulators stay zero and their rows are
-          // never stored).  The copies, waits and barriers are the same in
-          // every build, so the waves of a workgroup stay in step.
-          auto kloop = [&](auto fa_c) {
-            constexpr int FA = decltype(fa_c)::value;
-            // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
-            auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
-            Frags<T, A_MN, B_MN> f0, f1;
-#pragma unroll
-            for (int q = 0; q < FM + FN; ++q)
-              if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
-            for (int kt = 0; kt < KT; ++kt) {
-              const char* cs = stage(kt);
-              const char* ns = stage(kt + 1);
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                  const int q = i * FN + j;
-                  if (i < FA) acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
-                  __builtin_amdgcn_sched_barrier(0);
-                  if (q < FM + FN) {
-                    if (need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-                  } else if (q - (FM + FN) < DMA_PER_OP) {
-                    issue1(kt + STAGES - 1, q - (FM + FN));
-                  }
-                  __builtin_amdgcn_sched_barrier(0);
-                }
-              // K step kt+1 has landed once at most the copies issued after it
-              // (step kt+2, and step kt+3's A copies) are outstanding; the
-              // barrier extends that to all waves and retires every read of the
-              // stage refilled next
-              // (GLOOP: also step kt+3's indices, issued right after step
-              // kt+1's B copies, and one index copy more per step since)
-              wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
-              __syncthreads();
-              u32x4 ivn;
-              if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                  const int q = i * FN + j;
-                  if (i < FA) acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
-                  __builtin_amdgcn_sched_barrier(0);
-                  if (q < FM + FN) {
-                    if (need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-                  } else if (q - (FM + FN) < DMA_PER_OP) {
-                    if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
-                    else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-                  } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
-                    issue_idx(kt + STAGES + 1);
-                  }
-                  __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
+              __builtin_amdgcn_sched_barrier(0);
             }
-          };
-          const int rw = rows - wm * WTM;             // rows of the tile in this wave's half
-          const int fa = uniform(rw <= 0 ? 0 : min(FM, (rw + 31) / 32));
-          switch (fa) {
-            case 0: kloop(std::integral_constant<int, 0>{}); break;
-            case 1: kloop(std::integral_constant<int, 1>{}); break;
-            case 2: kloop(std::integral_constant<int, 2>{}); break;
-            case 3: kloop(std::integral_constant<int, 3>{}); break;
-            default: kloop(std::integral_constant<int, FM>{}); break;
-          }
+          // K step kt+1 has landed once at most the copies issued after it
+          // (step kt+2, and step kt+3's A copies) are outstanding; the
+          // barrier extends that to all waves and retires every read of the
+          // stage refilled next
+          // (GLOOP: also step kt+3's indices, issued right after step
+          // kt+1's B copies, and one index copy more per step since)
+          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+          __syncthreads();
+          u32x4 ivn;
+          if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+              else if (q - (FM + FN) < DMA_PER_OP) {
+                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
+                else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+              } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
+                issue_idx(kt + STAGES + 1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
         }
       } else {
         Frags<T, A_MN, B_MN> cur, nxt;
