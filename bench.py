@@ -101,15 +101,19 @@ def cpu_baseline(cfg_name, tokens, min_seconds=10.0, max_reps=8):
     cfg = synth.get_config(cfg_name, T=tokens)
     inp = synth.make_inputs(cfg)
     acc = np.float32 if cfg.dtype == "bf16" else np.float64
-    reps, spent = 0, 0.0
+    reps, spent, t_fwd, t_bwd = 0, 0.0, 0.0, 0.0
     while reps < max_reps and (reps == 0 or spent < min_seconds):
         t0 = time.perf_counter()
         fwd = oracle.layer_forward(inp.x, cfg.k, cfg.E, inp.w13, inp.w2, wg=inp.wg,
                                    bias=inp.bias, logits=inp.logits, g0=cfg.g0, G=cfg.G,
                                    ws13=inp.ws13, ws2=inp.ws2, acc=acc)
+        t1 = time.perf_counter()
         oracle.layer_backward(fwd, inp.dy, inp.x, inp.w13, inp.w2, wg=inp.wg, g0=cfg.g0,
                               G=cfg.G, ws13=inp.ws13, ws2=inp.ws2, acc=acc)
-        spent += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        spent += t2 - t0
         reps += 1
         del fwd
     try:
@@ -132,8 +136,11 @@ def cpu_baseline(cfg_name, tokens, min_seconds=10.0, max_reps=8):
         blas = "unknown"
     return {"value": tokens * reps / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{cfg_name} layer fwd+bwd on {tokens} tokens (same H/I/E/k and seeds as "
-                      f"the workload), numpy fp32 on bf16 inputs, {reps} repetitions, "
-                      f"{spent:.1f} s", "seconds": spent, "cpu": cpu_model, "blas": blas}
+                      f"the workload), numpy "
+                      + ("fp32 on bf16 inputs" if cfg.dtype == "bf16" else "fp64") +
+                      f", {reps} repetitions, "
+                      f"{spent:.1f} s", "seconds": spent, "forward_s_per_rep": t_fwd / reps,
+            "backward_s_per_rep": t_bwd / reps, "cpu": cpu_model, "blas": blas}
 
 
 def measured_traffic(call):
@@ -273,7 +280,9 @@ def main():
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     L.overlap = overlap
-    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+    # median over the steps of each call's event-to-event time
+    per_call = {c: float(np.median([ev[s][i].elapsed_time(ev[s][i + 1])
+                                    for s in range(args.steps)]))
                 for i, c in enumerate(calls)}
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / wall
