@@ -1,8 +1,8 @@
 // Softmax top-k routing and its backward ([CANN-MoE] s2.1: Softmax -> Top-k
 // -> mask, fused into one kernel).  One wavefront per token: each lane holds
 // the logits of experts lane, lane+64, ...; the row max and the exp-sum are
-// wave shuffle reductions, and each of the k selections is a wave arg-max
-// under the order (logit descending, expert index ascending).
+// wave shuffle reductions, and the top k under the order (logit descending,
+// expert index ascending) come from a radix select on ballots.
 #include "validate.hpp"
 
 #define ROUTE_WAVES 4           // tokens per workgroup
@@ -10,10 +10,22 @@
                                 // V = 1, 2, 4, 8, 16 logits per lane, the smallest
                                 // with 64 V >= E is launched)
 
-__device__ __forceinline__ bool route_better(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
+// Order-preserving key of a finite logit: larger logit <-> larger key; -0 is
+// taken as +0 so that equal logits have equal keys (ties go by index).
+__device__ __forceinline__ uint32_t route_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Top-k without cross-lane shuffles: the k-th largest key is found bit by bit
+// from the top (a key bit is kept when at least k keys reach the prefix with
+// it set; counts are wave ballots), the keys above it are chosen, and of the
+// keys equal to it the ones with the lowest expert index fill the rest.  The
+// slot of a chosen expert is the number of chosen experts ahead of it in the
+// order (logit descending, index ascending) -- everything ahead of a chosen
+// expert is chosen too.  Padding lanes (index >= E) hold key 0, below every
+// finite logit's key, and k <= E.
 template <int V>
 __global__ __launch_bounds__(ROUTE_WAVES * MOE_WAVE) void route_fwd_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
@@ -23,49 +35,74 @@ __global__ __launch_bounds__(ROUTE_WAVES * MOE_WAVE) void route_fwd_kernel(
   if (t >= T) return;
   const float* row = logits + (long long)t * E;
   float v[V];
-  bool taken[V];
+  uint32_t key[V];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    int e = lane + i * MOE_WAVE;
+    const int e = lane + i * MOE_WAVE;
     v[i] = e < E ? row[e] : -INFINITY;
-    taken[i] = e >= E;
+    key[i] = e < E ? route_key(v[i]) : 0u;
     m = fmaxf(m, v[i]);
   }
   m = wave_max(m);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    int e = lane + i * MOE_WAVE;
+    const int e = lane + i * MOE_WAVE;
     if (e < E) s += expf(v[i] - m);
   }
   s = wave_sum(s);
   const float inv = 1.0f / s;
-  for (int j = 0; j < k; ++j) {
-    // best candidate of this lane
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+  // the k-th largest key
+  uint32_t K = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = K | (1u << b);
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      int e = lane + i * MOE_WAVE;
-      if (!taken[i] && route_better(v[i], e, bv, be)) { bv = v[i]; be = e; }
-    }
-    // wave arg-max
+    for (int i = 0; i < V; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= k) K = c;
+  }
+  // chosen: keys above K, then ties at K by ascending index (i, then lane)
+  int need = k;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, MOE_WAVE);
-      int oe = __shfl_xor(be, o, MOE_WAVE);
-      if (route_better(ov, oe, bv, be)) { bv = ov; be = oe; }
-    }
-    // be is now the same in every lane; the owner marks it taken
+  for (int i = 0; i < V; ++i) need -= __popcll(__ballot(key[i] > K));
+  const unsigned long long below = (1ull << lane) - 1ull;
+  bool sel[V];
+  unsigned long long bsel[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (lane + i * MOE_WAVE == be) taken[i] = true;
-    if (lane == 0) {
-      idx[(long long)t * k + j] = be;
-      gate[(long long)t * k + j] = expf(bv - m) * inv;
+  for (int i = 0; i < V; ++i) {
+    const unsigned long long tie = __ballot(key[i] == K);
+    sel[i] = key[i] > K || (key[i] == K && __popcll(tie & below) < need);
+    const int nt = __popcll(tie);
+    need -= need < nt ? need : nt;
+    bsel[i] = __ballot(sel[i]);
+  }
+  // slots: chosen experts ahead of each chosen one
+  int slot[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) slot[i] = 0;
+#pragma unroll
+  for (int i2 = 0; i2 < V; ++i2) {
+    unsigned long long bm = bsel[i2];
+    while (bm) {
+      const int l2 = __builtin_ctzll(bm);
+      bm &= bm - 1;
+      const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], l2);
+      const int e2 = l2 + i2 * MOE_WAVE;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + i * MOE_WAVE;
+        slot[i] += (k2 > key[i]) || (k2 == key[i] && e2 < e);
+      }
     }
   }
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    if (sel[i]) {
+      const int e = lane + i * MOE_WAVE;
+      idx[(long long)t * k + slot[i]] = e;
+      gate[(long long)t * k + slot[i]] = expf(v[i] - m) * inv;
+    }
 }
 
 template <int V>
