@@ -164,7 +164,9 @@ def test_permute_without_copy_writes_the_same_maps(abi):
 
 
 @pytest.mark.parametrize("name,over", [("small", {}), ("pangu", {"T": 2048}),
-                                       ("deepseek", {"T": 1024})])
+                                       ("deepseek", {"T": 1024}),
+                                       # the benchmark's workload at full size
+                                       ("pangu", {})])
 def test_recompute_layer_equals_saving_layer(name, over):
     cfg = synth.get_config(name, **over)
     print(f"[recompute] config={cfg.name} T={cfg.T}", flush=True)
