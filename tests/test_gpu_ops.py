@@ -46,7 +46,9 @@ ROUTE_CASES = [(64, 8, 2, "normal"), (300, 64, 6, "normal"), (257, 256, 8, "ties
                (100, 1024, 8, "normal"), (33, 1024, 1024, "normal"), (50, 1, 1, "normal"),
                (70, 5, 5, "ties"), (129, 200, 3, "ties"),
                # every per-lane width of the kernels: E = 100 (2), E = 400 (8)
-               (90, 100, 4, "ties"), (77, 400, 8, "normal")]
+               (90, 100, 4, "ties"), (77, 400, 8, "normal"),
+               # -0.0 and +0.0 are the same logit: ties broken by expert index
+               (64, 64, 8, "signed_zeros"), (40, 300, 20, "signed_zeros")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
@@ -54,6 +56,11 @@ def test_route_bit_exact_indices(abi, T, E, k, kind):
     r = _rng(T + E + k)
     if kind == "ties":
         logits = (r.integers(-3, 4, size=(T, E)) * 0.5).astype(np.float32)
+    elif kind == "signed_zeros":
+        # mostly zeros of either sign, a few +-1: the k-th place falls among zeros
+        vals = np.array([-0.0, 0.0, -0.0, 0.0, -1.0, 1.0], np.float32)
+        logits = vals[r.integers(0, len(vals), size=(T, E))]
+        assert np.signbit(logits[logits == 0]).any() and (~np.signbit(logits[logits == 0])).any()
     else:
         logits = r.standard_normal((T, E)).astype(np.float32) * 2
     L = dev(logits, torch.float32)
