@@ -357,7 +357,7 @@ __device__ __forceinline__ float swiglu_act(float g, float u) {
 }
 
 // ---------------------------------------------------------------- the kernel
-template <typename T, int MODE, bool GATHER = false>
+template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
 __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   // DW with gathered Q rows: the rows change every K step, so each wave also
@@ -366,6 +366,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr bool GLOOP = GATHER && MODE == DW;
   constexpr int GI = GLOOP ? 1 : 0;
   static_assert(!GATHER || MODE == FWD1 || MODE == DW, "rows are gathered in FWD1 and DW");
+  static_assert(!LIGHT || (MODE != DW && sizeof(T) == 2), "light builds: bf16 row-tiled modes");
   static_assert(!GLOOP || sizeof(T) == 2, "gathered DW is built for bf16");
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
@@ -406,6 +407,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   __syncthreads();
   int total;
   int MBt = 0, NBt = 0;
+  bool light = false;   // LIGHT builds: the per-fragment-count loops are in use
   if constexpr (MODE != DW) {
     if (wave == 0) {
       const int per = (ng + 63) / 64;
@@ -429,6 +431,26 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
     const int nb = (MODE == FWD1) ? (a.I + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
     NBt = nb;
     total = g_pre[ng] * nb;
+    if constexpr (LIGHT) {
+      // light builds in use where at least half of the M-tiles are light (a
+      // group's last M-tile holding at most 64 rows): a few light tiles among
+      // full ones finish early, let some XCDs run ahead of the others and
+      // widen the stretch of operand panels the chip works on (HBM reads of
+      // the Pangu share's launches grew by 7-63% for no gain in time)
+      if (wave == 0) {
+        int lt = 0;
+        for (int g = lane; g < ng; g += 64) {
+          const int r = g_hi[g] - g_lo[g];
+          lt += (r > 0 && r - (r - 1) / BM * BM <= 64);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 64);
+        if (lane == 0) s_next = lt;   // (s_next is free until the first epilogue)
+      }
+      __syncthreads();
+      light = 2 * s_next >= g_pre[ng];
+      __syncthreads();   // s_next is written again at the first epilogue
+    }
   } else {
     // stable order by descending row count: g_pre[rank] = g
     for (int g = tid; g < ng; g += NT) {
@@ -699,48 +721,110 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
         // halves measured ~10% fewer cycles per step than issuing them
         // together).  Steps past the end
         // copy through the empty descriptor, so every step looks the same.
-        Frags<T, A_MN, B_MN> f0, f1;
-        f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
-        for (int kt = 0; kt < KT; ++kt) {
-          const char* cs = stage(kt);
-          const char* ns = stage(kt + 1);
+        // LIGHT builds: the loop is built per count FA of this wave's A
+        // fragments that hold rows of the tile; in a tile of a group with few
+        // rows the upper fragments (and the lower waves) see padding only, so
+        // their MFMAs and A-fragment reads are left out (their accumulators
+        // stay zero and their rows are never stored).  Copies, waits and
+        // barriers are the same in every build, so the waves of a workgroup
+        // stay in step, and every output is the same bits as without.
+        auto kloop = [&](auto fa_c) {
+          constexpr int FA = decltype(fa_c)::value;
+          // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
+          auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
+          Frags<T, A_MN, B_MN> f0, f1;
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
+          for (int q = 0; q < FM + FN; ++q)
+            if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
+          for (int kt = 0; kt < KT; ++kt) {
+            const char* cs = stage(kt);
+            const char* ns = stage(kt + 1);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int q = i * FN + j;
-              acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
-              __builtin_amdgcn_sched_barrier(0);
-              if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          // K step kt+1 has landed once at most the copies issued after it
-          // (step kt+2, and step kt+3's A copies) are outstanding; the
-          // barrier extends that to all waves and retires every read of the
-          // stage refilled next
-          // (GLOOP: also step kt+3's indices, issued right after step
-          // kt+1's B copies, and one index copy more per step since)
-          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
-          __syncthreads();
-          u32x4 ivn;
-          if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int q = i * FN + j;
-              acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
-              __builtin_amdgcn_sched_barrier(0);
-              if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-              else if (q - (FM + FN) < DMA_PER_OP) {
-                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
-                else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-              } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
-                issue_idx(kt + STAGES + 1);
+              for (int j = 0; j < FN; ++j) {
+                const int q = i * FN + j;
+                if (i < FA) acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < FM + FN) {
+                  if (need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+                } else if (q - (FM + FN) < DMA_PER_OP) {
+                  issue1(kt + STAGES - 1, q - (FM + FN));
+                }
+                __builtin_amdgcn_sched_barrier(0);
               }
-              __builtin_amdgcn_sched_barrier(0);
-            }
+            wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int q = i * FN + j;
+                if (i < FA) acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < FM + FN) {
+                  if (need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+                } else if (q - (FM + FN) < DMA_PER_OP) {
+                  issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+          }
+        };
+        if constexpr (LIGHT) {
+          const int rw = rows - wm * WTM;             // rows of the tile in this wave's half
+          const int fa = light ? uniform(rw <= 0 ? 0 : min(FM, (rw + 31) / 32)) : FM;
+          switch (fa) {
+            case 0: kloop(std::integral_constant<int, 0>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, FM>{}); break;
+          }
+        } else {
+          Frags<T, A_MN, B_MN> f0, f1;
+          f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
+          for (int kt = 0; kt < KT; ++kt) {
+            const char* cs = stage(kt);
+            const char* ns = stage(kt + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int q = i * FN + j;
+                acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+                else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            // K step kt+1 has landed once at most the copies issued after it
+            // (step kt+2, and step kt+3's A copies) are outstanding; the
+            // barrier extends that to all waves and retires every read of the
+            // stage refilled next
+            // (GLOOP: also step kt+3's indices, issued right after step
+            // kt+1's B copies, and one index copy more per step since)
+            wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+            __syncthreads();
+            u32x4 ivn;
+            if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int q = i * FN + j;
+                acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+                else if (q - (FM + FN) < DMA_PER_OP) {
+                  if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
+                  else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+                } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
+                  issue_idx(kt + STAGES + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+          }
         }
       } else {
         Frags<T, A_MN, B_MN> cur, nxt;
@@ -1063,18 +1147,31 @@ int grid_size() {
   return n >= 8 ? (n / 8) * 8 : n;
 }
 
-template <typename T, int MODE, bool GATHER = false>
+template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
-  hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER>), dim3(grid_size()), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER, LIGHT>), dim3(grid_size()), dim3(NT), 0, s, a);
   return moe_check_launch(what);
 }
 
+// light: launch the build with the per-fragment-count loops (row-tiled bf16
+// modes), for calls whose groups average at most half a tile of rows
 template <int MODE>
-int launch_dt(int dt, const GmmArgs& a, hipStream_t s, const char* what) {
+int launch_dt(int dt, const GmmArgs& a, hipStream_t s, const char* what, bool light = false) {
+  if constexpr (MODE != DW) {
+    if (light && dt == MOE_BF16) {
+      if constexpr (MODE == FWD1)
+        if (a.gather != nullptr) return launch<bf16_t, MODE, true, true>(a, s, what);
+      return launch<bf16_t, MODE, false, true>(a, s, what);
+    }
+  }
   if constexpr (MODE == FWD1 || MODE == DW)
     if (a.gather != nullptr) return launch<bf16_t, MODE, true>(a, s, what);   // bf16 only
   return dt == MOE_BF16 ? launch<bf16_t, MODE>(a, s, what) : launch<float, MODE>(a, s, what);
 }
+
+// Groups of a call that average at most half a 256-row tile: most of their
+// tiles are mostly padding (DeepSeek-like routing over many experts).
+bool small_groups(int G, int R) { return G > 0 && (long long)R <= (long long)G * (BM / 2); }
 
 // Checks of a row gather from the token matrix x [T, H] (recompute variant).
 int gather_checks(const char* fn, int dt, const void* x, const int32_t* src_token, int T, int H) {
@@ -1177,7 +1274,7 @@ int fwd_impl(const char* fn, const void* xp, const int32_t* gather, int gather_r
   a.C = h13; a.ldc = 2 * I;
   a.C2 = act; a.ldc2 = I;
   if (use_sh) { a.sX = sh->x; a.sW = sh->w13; a.sC = sh->h13; a.sC2 = sh->act; }
-  MOE_TRY(launch_dt<FWD1>(dt, a, s, fn));
+  MOE_TRY(launch_dt<FWD1>(dt, a, s, fn, small_groups(a.G, R)));
   // FWD2: yp = act . W2^T (N = H, K = I)
   a.gather = nullptr;
   a.N = H; a.K = I;
@@ -1186,7 +1283,7 @@ int fwd_impl(const char* fn, const void* xp, const int32_t* gather, int gather_r
   a.C = yp; a.ldc = H;
   a.C2 = nullptr;
   if (use_sh) { a.sX = sh->act; a.sW = sh->w2; a.sC = sh->y; a.sC2 = nullptr; }
-  return launch_dt<FWD2>(dt, a, s, fn);
+  return launch_dt<FWD2>(dt, a, s, fn, small_groups(a.G, R));
 }
 
 }  // namespace
@@ -1247,7 +1344,7 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
   a.C = dh13; a.ldc = 2 * I;
   a.aux = h13; a.ldaux = 2 * I;
   if (use_sh) { a.sX = sh->dy; a.sW = sh->w2; a.sC = sh->dh13; a.sAux = sh->h13; }
-  MOE_TRY(launch_dt<DX1>(dt, a, s, fn));
+  MOE_TRY(launch_dt<DX1>(dt, a, s, fn, small_groups(a.G, R)));
   // DX2: dxp = dh13 . W13 (W13 stored [K=2I][N=H])
   a.N = H; a.K = 2 * I;
   a.X = dh13; a.ldx = 2 * I;
@@ -1255,7 +1352,7 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
   a.C = dxp; a.ldc = H;
   a.aux = nullptr;
   if (use_sh) { a.sX = sh->dh13; a.sW = sh->w13; a.sC = sh->dx; a.sAux = nullptr; }
-  return launch_dt<DX2>(dt, a, s, fn);
+  return launch_dt<DX2>(dt, a, s, fn, small_groups(a.G, R));
 }
 
 namespace {

@@ -317,3 +317,42 @@ def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt, dynamic):
         for t in (yp, dxp, h13):
             hv = host(t)
             assert not hv[:lo].any() and not hv[hi:].any()
+
+
+def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi):
+    """Calls whose groups average at most half a tile of rows launch the
+    builds that skip the MFMAs of padding fragments.  The same groups with a
+    larger row count R (so the host picks the full-tile builds) give the same
+    bits in every output row."""
+    r = _rng(4242)
+    counts = [int(c) for c in r.integers(0, 90, 96)]
+    counts[5], counts[17] = 0, 300          # an empty group and a multi-tile one
+    G, H, I = len(counts), 512, 256
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    R = int(offsets[-1])
+    assert R <= G * 128                     # small groups: light builds
+    R_big = G * 256 + 1                     # same groups, full-tile builds
+    xp = _store(r.standard_normal((R_big, H)), "bf16")
+    dyp = _store(r.standard_normal((R_big, H)), "bf16")
+    w13 = _store(r.standard_normal((G, 2 * I, H)) * 0.05, "bf16")
+    w2 = _store(r.standard_normal((G, H, I)) * 0.05, "bf16")
+    tdt, code = torch.bfloat16, abi.MOE_BF16
+    OFF = dev(offsets, torch.int32)
+    XP, DYP, W13, W2 = dev(xp, tdt), dev(dyp, tdt), dev(w13, tdt), dev(w2, tdt)
+    wsb = abi.moe_gmm_workspace_bytes()
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for rows in (R, R_big):
+        h13 = torch.zeros(R_big, 2 * I, dtype=tdt, device="cuda")
+        act = torch.zeros(R_big, I, dtype=tdt, device="cuda")
+        yp = torch.zeros(R_big, H, dtype=tdt, device="cuda")
+        dh13 = torch.zeros(R_big, 2 * I, dtype=tdt, device="cuda")
+        dxp = torch.zeros(R_big, H, dtype=tdt, device="cuda")
+        abi.moe_grouped_gemm_fwd(XP, OFF, 0, G, rows, code, H, I, W13, W2, h13, act, yp, None,
+                                 ws, wsb)
+        abi.moe_grouped_gemm_bwd_dx(DYP, OFF, 0, G, rows, code, H, I, W13, W2, h13, dh13, dxp,
+                                    None, ws, wsb)
+        torch.cuda.synchronize()
+        outs.append([t[:R].clone() for t in (h13, act, yp, dh13, dxp)])
+    for name, a, b in zip(("h13", "act", "yp", "dh13", "dxp"), outs[0], outs[1]):
+        assert torch.equal(a, b), name
