@@ -323,7 +323,8 @@ def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi):
     """Calls whose groups average at most half a tile of rows launch the
     builds that skip the MFMAs of padding fragments.  The same groups with a
     larger row count R (so the host picks the full-tile builds) give the same
-    bits in every output row."""
+    bits in every output row, also through the gathering forward (which
+    matches the forward on the gathered rows bit for bit)."""
     r = _rng(4242)
     counts = [int(c) for c in r.integers(0, 90, 96)]
     counts[5], counts[17] = 0, 300          # an empty group and a multi-tile one
@@ -338,6 +339,7 @@ def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi):
     w2 = _store(r.standard_normal((G, H, I)) * 0.05, "bf16")
     tdt, code = torch.bfloat16, abi.MOE_BF16
     OFF = dev(offsets, torch.int32)
+    SRC = dev(np.arange(R_big), torch.int32)
     XP, DYP, W13, W2 = dev(xp, tdt), dev(dyp, tdt), dev(w13, tdt), dev(w2, tdt)
     wsb = abi.moe_gmm_workspace_bytes()
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
@@ -352,7 +354,16 @@ def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi):
                                  ws, wsb)
         abi.moe_grouped_gemm_bwd_dx(DYP, OFF, 0, G, rows, code, H, I, W13, W2, h13, dh13, dxp,
                                     None, ws, wsb)
+        # the gathering forward, with row r reading token r (so its inputs are xp's)
+        gh13 = torch.zeros(R_big, 2 * I, dtype=tdt, device="cuda")
+        gact = torch.zeros(R_big, I, dtype=tdt, device="cuda")
+        gyp = torch.zeros(R_big, H, dtype=tdt, device="cuda")
+        abi.moe_grouped_gemm_fwd_gather(XP, SRC, R_big, OFF, 0, G, rows, code, H, I, W13, W2,
+                                        gh13, gact, gyp, None, ws, wsb)
         torch.cuda.synchronize()
-        outs.append([t[:R].clone() for t in (h13, act, yp, dh13, dxp)])
-    for name, a, b in zip(("h13", "act", "yp", "dh13", "dxp"), outs[0], outs[1]):
+        outs.append([t[:R].clone() for t in (h13, act, yp, dh13, dxp, gh13, gact, gyp)])
+    names = ("h13", "act", "yp", "dh13", "dxp", "gather h13", "gather act", "gather yp")
+    for name, a, b in zip(names, outs[0], outs[1]):
         assert torch.equal(a, b), name
+    for a, b in zip(outs[0][:3], outs[0][5:]):
+        assert torch.equal(a, b)
