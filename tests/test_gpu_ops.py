@@ -138,6 +138,14 @@ def test_permute_bit_exact(abi, T, E, k, H, dt):
     assert np.array_equal(host(rmap), rm)
     assert np.array_equal(host(src), rs)
     assert np.array_equal(host(xp), rxp)          # a bit copy of bf16/fp32 values
+    # a second call on the same workspace (outputs cleared) gives the same maps
+    for t in (counts, offsets, rmap, src):
+        t.fill_(-1)
+    abi.moe_permute(X, _code(abi, dt), dev(idx, torch.int32), T, H, E, k, xp, counts, offsets,
+                    rmap, src, ws, wsb)
+    torch.cuda.synchronize()
+    for got, ref in ((counts, rc), (offsets, ro), (rmap, rm), (src, rs)):
+        assert np.array_equal(host(got), ref)
 
 
 @pytest.mark.parametrize("T,E,k,H,dt", PERM_CASES)
