@@ -327,15 +327,22 @@ def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt, dynamic):
             assert not hv[:lo].any() and not hv[hi:].any()
 
 
-def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi):
+@pytest.mark.parametrize("kind", ["light_tiles", "half_tiles"])
+def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi, kind):
     """Calls whose groups average at most half a tile of rows launch the
     builds that skip the MFMAs of padding fragments.  The same groups with a
     larger row count R (so the host picks the full-tile builds) give the same
     bits in every output row, also through the gathering forward (which
-    matches the forward on the gathered rows bit for bit)."""
+    matches the forward on the gathered rows bit for bit).  light_tiles:
+    most tiles hold at most 64 rows, so the waves take the short loops;
+    half_tiles: every group holds 65-128 rows, so the small-group build runs
+    its full loop (the device-side choice declines the short ones)."""
     r = _rng(4242)
-    counts = [int(c) for c in r.integers(0, 90, 96)]
-    counts[5], counts[17] = 0, 300          # an empty group and a multi-tile one
+    if kind == "light_tiles":
+        counts = [int(c) for c in r.integers(0, 90, 96)]
+        counts[5], counts[17] = 0, 300      # an empty group and a multi-tile one
+    else:
+        counts = [int(c) for c in r.integers(65, 129, 96)]
     G, H, I = len(counts), 512, 256
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     R = int(offsets[-1])
