@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd+bwd tokens/s on 1 GPU; GMM % MFMA peak; permute % HBM BW"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FLUSH_BYTES = 1 << 30          # scratch read before each call of the per-call breakdown
 
 
 def parse():
@@ -48,6 +49,8 @@ def parse():
                         "always measured that way)")
     p.add_argument("--cpu-tokens", type=int, default=8192,
                    help="tokens in the oracle's timed sample")
+    p.add_argument("--no-dense-ref", action="store_true",
+                   help="skip timing torch.matmul (hipBLASLt) on the dense equivalents")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device-to-device copy of this many MiB before the timed "
                         "region (a known-size reference for HBM byte counters)")
@@ -143,6 +146,55 @@ def cpu_baseline(cfg_name, tokens, min_seconds=10.0, max_reps=8):
             "backward_s_per_rep": t_bwd / reps, "cpu": cpu_model, "blas": blas}
 
 
+def dense_reference(cfg, reps=10):
+    """The library bar for the grouped GEMM: torch.matmul (hipBLASLt) in bf16
+    on the dense products of one expert that receives all T tokens (for the
+    Pangu share: exactly the shared expert's six products), operands in the
+    layouts the layer stores them in.  Reports TFLOP/s per product and per
+    call (the call's two products back to back)."""
+    import torch
+    T, H, I = cfg.T, cfg.H, cfg.I
+    bf = torch.bfloat16
+    r = lambda *shp: torch.randn(*shp, device="cuda", dtype=bf)
+    x, dy, act, dh13 = r(T, H), r(T, H), r(T, I), r(T, 2 * I)
+    w13, w2 = r(2 * I, H), r(H, I)
+    prods = {
+        "fwd1": (lambda: x @ w13.t(), 2.0 * T * 2 * I * H),     # h13 = x W13^T
+        "fwd2": (lambda: act @ w2.t(), 2.0 * T * H * I),        # y = act W2^T
+        "dx1": (lambda: dy @ w2, 2.0 * T * I * H),              # dact = dy W2
+        "dx2": (lambda: dh13 @ w13, 2.0 * T * H * 2 * I),       # dx = dh13 W13
+        "dw2": (lambda: dy.t() @ act, 2.0 * H * I * T),         # dW2 = dy^T act
+        "dw13": (lambda: dh13.t() @ x, 2.0 * 2 * I * H * T),    # dW13 = dh13^T x
+    }
+    ms = {}
+    for n, (fn, _) in prods.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[n] = e0.elapsed_time(e1) / reps
+    out = {"what": f"torch.matmul (hipBLASLt) bf16, dense products of one expert on all "
+                   f"{T} tokens (H={H}, I={I}), operands in the layer's layouts",
+           "products": {n: {"ms": round(ms[n], 4),
+                            "tflops": round(f / (ms[n] * 1e-3) / 1e12, 1),
+                            "frac_bf16_peak": round(f / (ms[n] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                        for n, (_, f) in prods.items()}}
+    for call, (a, b) in {"gmm_fwd": ("fwd1", "fwd2"), "gmm_bwd_dx": ("dx1", "dx2"),
+                         "gmm_bwd_dw": ("dw2", "dw13")}.items():
+        t = ms[a] + ms[b]
+        tf = 6.0 * T * H * I / (t * 1e-3) / 1e12
+        out[call] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del x, dy, act, dh13, w13, w2
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(call):
     """HBM bytes per launch of ``call`` from the committed rocprofv3 byte
     counters, if they were taken on the current kernel source (else None)."""
@@ -228,8 +280,7 @@ def main():
     import torch
 
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import make_layer
+    from synth.device import make_layer
 
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.config)
@@ -267,21 +318,30 @@ def main():
     wall = t1 - t0
 
     # per-call breakdown: the same steps with every call on the working
-    # stream, HIP events between the calls
+    # stream; before each call a 1 GiB scratch read streams through the 256 MB
+    # last-level cache (MALL) and the L2s, so no call reads its inputs from
+    # the cache its predecessor left warm (a read, not a write: the lines it
+    # leaves are clean, so the timed call does not pay for writing back the
+    # flush; the predecessor's own dirty lines are written back during it);
+    # HIP events bracket the call alone
     overlap, L.overlap = L.overlap, False
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-          for _ in range(args.steps)]
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(len(calls))] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
-        ev[s][0].record(stream)
         for i, c in enumerate(calls):
+            torch.amax(flush, dim=0, out=sink)
+            ev[s][i][0].record(stream)
             getattr(L, c)()
-            ev[s][i + 1].record(stream)
+            ev[s][i][1].record(stream)
     torch.cuda.synchronize()
+    del flush, sink
     L.overlap = overlap
     # median over the steps of each call's event-to-event time
-    per_call = {c: float(np.median([ev[s][i].elapsed_time(ev[s][i + 1])
+    per_call = {c: float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1])
                                     for s in range(args.steps)]))
                 for i, c in enumerate(calls)}
     ms_per_step = wall * 1e3 / args.steps
@@ -324,6 +384,8 @@ def main():
         "roofline": roof,
         "phases": phases,
     }
+    if not args.no_dense_ref and cfg.dtype == "bf16":
+        out["dense_ref"] = dense_reference(cfg)
     if not args.no_variants and cfg.dtype == "bf16":
         import math
         C = math.ceil(1.2 * cfg.T * cfg.k / cfg.E)   # capacity factor 1.2
