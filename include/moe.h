@@ -156,6 +156,23 @@ int moe_permute(const void* x, int dt, const int32_t* idx, int T, int H, int E, 
 int moe_load_stats(const int32_t* counts, int E, int experts_per_group, float* load, float* cv,
                    int32_t* group_counts, moe_stream_t stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, outputs and bits as moe_permute, without the workspace
+ * arguments.  Its rank workspace is a file-scope device array of
+ * moe_permute_noalloc_max_scratch_bytes() bytes (4 MiB) that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing.
+ * Limit: moe_permute_workspace_bytes(T, E, k) must not exceed that size
+ * (T*k up to 2^24 pairs at E = 256, 2^22 at E = 1024); larger shapes get
+ * MOE_ERR_UNSUPPORTED.  Every call on one GPU uses that GPU's one array, so
+ * calls that overlap on one GPU (different streams, no ordering between them)
+ * race and give wrong maps; calls ordered on one stream are safe.
+ */
+size_t moe_permute_noalloc_max_scratch_bytes(void);
+int moe_permute_noalloc(const void* x, int dt, const int32_t* idx, int T, int H, int E, int k,
+                        void* xp, int32_t* counts, int32_t* offsets, int32_t* row_id_map,
+                        int32_t* src_token, moe_stream_t stream);
+
 /* Drop-and-pad permute, the variant the pages compare dropless training with
  * ([CANN-MoE] s4.3 capacity factor 1.2; [Pangu-QA] MoE training analysis):
  * every expert owns C rows, R = E*C (C = ceil(factor * T*k / E) for a

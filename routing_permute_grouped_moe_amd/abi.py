@@ -53,6 +53,8 @@ _SIGS = {
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc_max_scratch_bytes": (_SZ, []),
+    "moe_permute_noalloc": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_load_stats": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "moe_permute_capacity": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                   _P]),
@@ -158,6 +160,16 @@ def moe_permute(x, dt, idx, T, H, E, k, xp, counts, offsets, row_id_map, src_tok
                 ws_bytes, stream=None):
     _call("moe_permute", addr(x), dt, addr(idx), T, H, E, k, addr(xp), addr(counts),
           addr(offsets), addr(row_id_map), addr(src_token), addr(ws), ws_bytes, _stream(stream))
+
+
+def moe_permute_noalloc_max_scratch_bytes() -> int:
+    return _lib.moe_permute_noalloc_max_scratch_bytes()
+
+
+def moe_permute_noalloc(x, dt, idx, T, H, E, k, xp, counts, offsets, row_id_map, src_token,
+                        stream=None):
+    _call("moe_permute_noalloc", addr(x), dt, addr(idx), T, H, E, k, addr(xp), addr(counts),
+          addr(offsets), addr(row_id_map), addr(src_token), _stream(stream))
 
 
 def moe_load_stats(counts, E, experts_per_group, load, cv, group_counts, stream=None):

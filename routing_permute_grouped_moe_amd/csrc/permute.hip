@@ -17,6 +17,8 @@
 //
 // The row moves are token-centric: one workgroup per token reads the token's
 // row once with 16-byte lanes and writes (or gathers) its k rows.
+#include <mutex>
+
 #include "validate.hpp"
 
 #define RANK_WAVES 16      // wavefronts of a rank workgroup
@@ -637,6 +639,58 @@ extern "C" int moe_permute(const void* x, int dt, const int32_t* idx, int T, int
                            int32_t* src_token, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return permute_impl("moe_permute", x, dt, idx, T, H, E, k, -1, xp, counts, offsets, row_id_map,
                       src_token, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation permute
+// moe_permute with its rank workspace in a file-scope device array instead of
+// a caller buffer, for callers that cannot allocate.  The array lives on every
+// device the library runs on until the process ends; the rank kernel writes
+// every entry a call reads, so nothing has to start at zero.
+constexpr long long NOALLOC_SCRATCH_BYTES = 4LL << 20;
+static __device__ __align__(256) int32_t scratch[NOALLOC_SCRATCH_BYTES / 4];
+
+// Device address of ``scratch`` on the current device, looked up once per
+// device (the array's name is only a host-side stand-in for it).
+static int scratch_address(const char* fn, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return moe_fail(MOE_ERR_LAUNCH, "%s: no current HIP device", fn);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return moe_fail(MOE_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", fn,
+                      hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+extern "C" size_t moe_permute_noalloc_max_scratch_bytes(void) {
+  return (size_t)NOALLOC_SCRATCH_BYTES;
+}
+
+extern "C" int moe_permute_noalloc(const void* x, int dt, const int32_t* idx, int T, int H, int E,
+                                   int k, void* xp, int32_t* counts, int32_t* offsets,
+                                   int32_t* row_id_map, int32_t* src_token,
+                                   moe_stream_t stream) {
+  const char* fn = "moe_permute_noalloc";
+  MOE_TRY(row_checks(fn, dt, T, H, k));
+  MOE_TRY(moe_need_ek(E, k, fn));
+  const size_t need = moe_permute_workspace_bytes(T, E, k);
+  if (need > (size_t)NOALLOC_SCRATCH_BYTES)
+    return moe_fail(MOE_ERR_UNSUPPORTED,
+                    "%s: T = %d, E = %d, k = %d need %zu bytes of rank scratch, above the %lld "
+                    "this entry point holds (use moe_permute with a workspace)",
+                    fn, T, E, k, need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (T > 0) MOE_TRY(scratch_address(fn, &ws));
+  return permute_impl(fn, x, dt, idx, T, H, E, k, -1, xp, counts, offsets, row_id_map, src_token,
+                      ws, (size_t)NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int moe_permute_capacity(const void* x, int dt, const int32_t* idx, int T, int H, int E,

@@ -162,3 +162,17 @@ def test_binding_raises_with_detail(abi):
         abi.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, stream=0)
     assert ei.value.status == abi.MOE_ERR_UNSUPPORTED
     assert "k = 9" in str(ei.value)
+
+
+def test_noalloc_permute_size_limit(abi):
+    # 4 MiB of rank scratch: T*k = 2^24 pairs at E = 256 fit exactly, one
+    # block more does not; the limit is checked on the host before any HIP call
+    assert abi.moe_permute_noalloc_max_scratch_bytes() == 4 << 20
+    assert abi.moe_permute_workspace_bytes(1 << 21, 256, 8) == 4 << 20
+    st = status(abi, "moe_permute_noalloc", FAKE, 1, FAKE, (1 << 21) + 1, 128, 256, 8, FAKE,
+                FAKE, FAKE, FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED and "moe_permute with a workspace" in abi.moe_last_error()
+    # the other host checks still apply
+    st = status(abi, "moe_permute_noalloc", FAKE, 1, FAKE, 100, 100, 8, 2, FAKE, FAKE, FAKE,
+                FAKE, FAKE, None)
+    assert st == abi.MOE_ERR_UNSUPPORTED
