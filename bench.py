@@ -57,8 +57,12 @@ def parse():
     return p.parse_args()
 
 
-CALLS = ["router_fwd", "route", "permute", "load_stats", "gmm_fwd", "combine", "combine_bwd", "gmm_bwd_dx",
-         "gmm_bwd_dw", "route_bwd", "router_bwd", "permute_bwd"]
+# the calls of one step, in order; the dX and dW products run in one call
+# (gmm_bwd); gmm_bwd_dx and gmm_bwd_dw, its two halves as separate calls,
+# are timed after the step's calls for reference
+CALLS = ["router_fwd", "route", "permute", "load_stats", "gmm_fwd", "combine", "combine_bwd",
+         "gmm_bwd", "route_bwd", "router_bwd", "permute_bwd"]
+REFERENCE_CALLS = ["gmm_bwd_dx", "gmm_bwd_dw"]
 
 
 def algorithmic(cfg, rows_local, active_local):
@@ -85,6 +89,8 @@ def algorithmic(cfg, rows_local, active_local):
         "combine_bwd": {"bytes": T * H * b + 2.0 * T * k * H * b + 12.0 * T * k},
         "gmm_bwd_dx": {"flops": gmm_flops, "bytes": w_read + rows * (2 * H + 4 * I) * b},
         "gmm_bwd_dw": {"flops": gmm_flops, "bytes": w_write + rows * (2 * H + 3 * I) * b},
+        "gmm_bwd": {"flops": 2 * gmm_flops,
+                    "bytes": w_read + w_write + rows * (4 * H + 7 * I) * b},
         "route_bwd": {"bytes": 8.0 * T * E + 12.0 * T * k},
         "router_bwd": {"flops": 4.0 * T * H * E, "bytes": 2 * T * H * b + H * E * 4 + T * E * 4},
         "permute_bwd": {"bytes": (k + 1) * T * H * b + 4.0 * T * k
@@ -328,11 +334,12 @@ def main():
     stream = torch.cuda.current_stream()
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
+    timed = calls + REFERENCE_CALLS
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(len(calls))] for _ in range(args.steps)]
+           for _ in range(len(timed))] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
-        for i, c in enumerate(calls):
+        for i, c in enumerate(timed):
             torch.amax(flush, dim=0, out=sink)
             ev[s][i][0].record(stream)
             getattr(L, c)()
@@ -343,13 +350,13 @@ def main():
     # median over the steps of each call's event-to-event time
     per_call = {c: float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1])
                                     for s in range(args.steps)]))
-                for i, c in enumerate(calls)}
+                for i, c in enumerate(timed)}
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / wall
 
     alg = algorithmic(cfg, rows_local, active_local)
     phases = {}
-    for c in calls:
+    for c in timed:
         ms = per_call[c]
         d = {"ms": round(ms, 4)}
         if "flops" in alg[c]:

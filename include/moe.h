@@ -296,6 +296,23 @@ int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp, co
                             void* dw13, void* dw2, const moe_shared_expert* shared,
                             void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* dX and dW in one call: the outputs of moe_grouped_gemm_bwd_dx followed by
+ * moe_grouped_gemm_bwd_dw (same arguments, same bits), computed in two
+ * persistent launches that each pair one dX product with the weight-gradient
+ * product that does not depend on it -- [dact + SwiGLU bwd | dw2], then
+ * [dxp | dw13] -- so the weight-gradient tiles fill the rounds the dX
+ * products leave partly idle.  [Pangu-QA] keeps dW apart from dX so that dW
+ * can overlap communication; on one GPU it overlaps the dX products instead.
+ * Shapes the paired launches do not cover (a shared expert with no rows, no
+ * routed rows, groups averaging half a tile or less) run the two calls'
+ * launches.  Same workspace as the other grouped-GEMM calls.
+ */
+int moe_grouped_gemm_bwd(const void* xp, const void* act, const void* dyp,
+                         const int32_t* offsets, int g0, int G, int R, int dt, int H, int I,
+                         const void* w13, const void* w2, const void* h13, void* dh13,
+                         void* dxp, void* dw13, void* dw2, const moe_shared_expert* shared,
+                         void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* ---------------------------------------------------------------- recompute variant
  * Fine-grained recompute in place of saved activations ([Pangu-QA], the
  * memory-saving part: modules such as the permute and the activation

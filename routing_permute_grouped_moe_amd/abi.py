@@ -69,6 +69,8 @@ _SIGS = {
                                      ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
     "moe_grouped_gemm_bwd_dw": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                      ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
+    "moe_grouped_gemm_bwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                  _P, ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
     "moe_grouped_gemm_fwd_gather": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
                                          _P, ctypes.POINTER(SharedExpert), _P, _SZ, _P]),
     "moe_grouped_gemm_bwd_dw_recompute": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -237,6 +239,13 @@ def moe_grouped_gemm_bwd_dw(xp, act, dyp, dh13, offsets, g0, G, R, dt, H, I, dw1
     _call("moe_grouped_gemm_bwd_dw", addr(xp), addr(act), addr(dyp), addr(dh13), addr(offsets),
           g0, G, R, dt, H, I, addr(dw13), addr(dw2), _sh(shared), addr(ws), ws_bytes,
           _stream(stream))
+
+
+def moe_grouped_gemm_bwd(xp, act, dyp, offsets, g0, G, R, dt, H, I, w13, w2, h13, dh13, dxp,
+                         dw13, dw2, shared=None, ws=None, ws_bytes=0, stream=None):
+    _call("moe_grouped_gemm_bwd", addr(xp), addr(act), addr(dyp), addr(offsets), g0, G, R, dt, H,
+          I, addr(w13), addr(w2), addr(h13), addr(dh13), addr(dxp), addr(dw13), addr(dw2),
+          _sh(shared), addr(ws), ws_bytes, _stream(stream))
 
 
 def moe_grouped_gemm_fwd_gather(x, src_token, T, offsets, g0, G, R, dt, H, I, w13, w2, h13, act,

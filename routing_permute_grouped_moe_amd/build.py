@@ -5,6 +5,7 @@ Run ``python -m routing_permute_grouped_moe_amd.build``; it always recompiles.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -23,13 +24,35 @@ FLAGS = [
 ]
 
 
+def _scratch_kernels(remarks: str):
+    """Kernels whose registers spill to scratch, from the compiler's resource
+    remarks (``Function Name`` followed by ``ScratchSize [bytes/lane]``)."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            bad.append((name, int(m.group(1))))
+    return bad
+
+
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *lang, "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    # The grouped GEMM counts its own buffer loads (hand-written waits on the
+    # vector-memory counter around the LDS copies); a kernel that spills
+    # registers to scratch adds memory operations of its own, and such a build
+    # has given wrong results.  No kernel of the library may spill.
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels spill registers to scratch: {bad}")
     return out
 
 

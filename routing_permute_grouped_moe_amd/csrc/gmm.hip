@@ -356,9 +356,128 @@ __device__ __forceinline__ float swiglu_act(float g, float u) {
   return g * sigmoidf_(g) * u;
 }
 
-// ---------------------------------------------------------------- the kernel
-template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
-__global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
+// ---------------------------------------------------------------- tile spaces
+// Group window of a launch in LDS (the products of one launch share it).
+struct GroupLds {
+  int lo[MOE_MAX_E + 2], hi[MOE_MAX_E + 2];   // clamped row ranges
+  int pre[MOE_MAX_E + 2];   // row-tiled products: M-tiles before each group, pre[ng] = all
+  int ord[MOE_MAX_E + 2];   // weight-gradient products: groups by descending row count
+};
+
+// Tile space of one product.
+struct Space {
+  int total;       // tiles
+  int MBt, NBt;    // DW: M and N tiles of a group; others: N tiles of a row tile
+  bool light;      // LIGHT builds: the per-fragment-count loops are in use
+};
+
+// Row ranges of the window's groups (and of the shared expert as group G).
+__device__ __forceinline__ void load_groups(const GmmArgs& a, GroupLds& gl) {
+  const int ng = a.G + a.shared;
+  for (int g = threadIdx.x; g < ng; g += NT) {
+    int lo, hi;
+    if (g < a.G && !a.dense) {
+      lo = a.offsets[a.g0 + g];
+      hi = a.offsets[a.g0 + g + 1];
+      lo = lo < 0 ? 0 : (lo > a.R ? a.R : lo);
+      hi = hi < lo ? lo : (hi > a.R ? a.R : hi);
+    } else {
+      lo = 0;
+      hi = a.shT;
+    }
+    gl.lo[g] = lo;
+    gl.hi[g] = hi;
+  }
+  __syncthreads();
+}
+
+// Per-group M-tile prefix (row-tiled modes) into gl.pre.
+__device__ __forceinline__ void tile_prefix(int ng, GroupLds& gl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    const int per = (ng + 63) / 64;
+    const int b0 = lane * per, b1 = min(ng, b0 + per);
+    int s = 0;
+    for (int g = b0; g < b1; ++g) s += (gl.hi[g] - gl.lo[g] + BM - 1) / BM;
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - s;
+    for (int g = b0; g < b1; ++g) {
+      gl.pre[g] = run;
+      run += (gl.hi[g] - gl.lo[g] + BM - 1) / BM;
+    }
+    if (lane == 63) gl.pre[ng] = incl;
+  }
+  __syncthreads();
+}
+
+// Group order by descending row count (stable) into gl.ord.
+__device__ __forceinline__ void group_order(int ng, GroupLds& gl) {
+  for (int g = threadIdx.x; g < ng; g += NT) {
+    const int c = gl.hi[g] - gl.lo[g];
+    int rank = 0;
+    for (int h = 0; h < ng; ++h) {
+      const int ch = gl.hi[h] - gl.lo[h];
+      rank += (ch > c) || (ch == c && h < g);
+    }
+    gl.ord[rank] = g;
+  }
+  __syncthreads();
+}
+
+// Tile space of a product whose group tables are in place (tile_prefix for
+// row-tiled modes, group_order for DW).  s_tmp: an LDS int free until the
+// first epilogue.
+template <int MODE, bool LIGHT>
+__device__ __forceinline__ Space tile_space(const GmmArgs& a, const GroupLds& gl, int* s_tmp) {
+  const int ng = a.G + a.shared;
+  Space sp;
+  sp.light = false;
+  if constexpr (MODE != DW) {
+    sp.MBt = 0;
+    sp.NBt = (MODE == FWD1) ? (a.I + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
+    sp.total = gl.pre[ng] * sp.NBt;
+    if constexpr (LIGHT) {
+      // light builds in use where at least half of the M-tiles are light (a
+      // group's last M-tile holding at most 64 rows): a few light tiles among
+      // full ones finish early, let some XCDs run ahead of the others and
+      // widen the stretch of operand panels the chip works on (HBM reads of
+      // the Pangu share's launches grew by 7-63% for no gain in time)
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      if (wave == 0) {
+        int lt = 0;
+        for (int g = lane; g < ng; g += 64) {
+          const int r = gl.hi[g] - gl.lo[g];
+          lt += (r > 0 && r - (r - 1) / BM * BM <= 64);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 64);
+        if (lane == 0) *s_tmp = lt;
+      }
+      __syncthreads();
+      sp.light = 2 * *s_tmp >= gl.pre[ng];
+      __syncthreads();
+    }
+  } else {
+    sp.MBt = (a.M + BM - 1) / BM;
+    sp.NBt = (a.N + BN - 1) / BN;
+    sp.total = ng * sp.MBt * sp.NBt;
+  }
+  return sp;
+}
+
+// ---------------------------------------------------------------- one tile
+// Tile tile_id of a product: main loop over K and epilogue.  smem is the
+// 128 KB operand ring (also the epilogue's staging), g_idx the gathered-row
+// index ring.  drained() runs once per tile, by every thread, at the point
+// where every copy of the tile and the scheduler's draw have landed.
+template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, typename Drained>
+__device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
+                                         int tile_id, char* smem, int* g_idx, Drained&& drained) {
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   // DW with gathered Q rows: the rows change every K step, so each wave also
   // copies its K rows' indices into an LDS ring, two steps before the copies
@@ -374,501 +493,441 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr int DMA_PER_OP = Cfg<T>::DPO;
   constexpr int DMA_PER_STEP = 2 * DMA_PER_OP;   // buffer loads per wave per K step
   static_assert(STAGES * STAGE_BYTES == RING_BYTES, "stage ring size");
-
-  __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
   static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
-  __shared__ int g_lo[MOE_MAX_E + 2], g_hi[MOE_MAX_E + 2], g_pre[MOE_MAX_E + 2];
-  __shared__ int g_kp[MOE_MAX_E + 2];   // DW: K steps before each group in work order
-  __shared__ int s_next;
-  // GLOOP: [wave][step % 4][64] row indices (lanes 0-7 of each copy carry them)
-  __shared__ __attribute__((aligned(16))) int g_idx[GLOOP ? (NT / 64) * 4 * 64 : 4];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 wave grid
   const int ng = a.G + a.shared;
-
-  // ---- group table: clamped row ranges, then per-group tile prefix (M-var
-  // modes) or the group order by descending row count (DW).
-  for (int g = tid; g < ng; g += NT) {
-    int lo, hi;
-    if (g < a.G && !a.dense) {
-      lo = a.offsets[a.g0 + g];
-      hi = a.offsets[a.g0 + g + 1];
-      lo = lo < 0 ? 0 : (lo > a.R ? a.R : lo);
-      hi = hi < lo ? lo : (hi > a.R ? a.R : hi);
-    } else {
-      lo = 0;
-      hi = a.shT;
-    }
-    g_lo[g] = lo;
-    g_hi[g] = hi;
-  }
-  __syncthreads();
-  int total;
-  int MBt = 0, NBt = 0;
-  bool light = false;   // LIGHT builds: the per-fragment-count loops are in use
+  // ---- locate the tile
+  int g, m0, n0, rows0 = 0, rows = 0, kdim;
   if constexpr (MODE != DW) {
-    if (wave == 0) {
-      const int per = (ng + 63) / 64;
-      const int b0 = lane * per, b1 = min(ng, b0 + per);
-      int s = 0;
-      for (int g = b0; g < b1; ++g) s += (g_hi[g] - g_lo[g] + BM - 1) / BM;
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      int run = incl - s;
-      for (int g = b0; g < b1; ++g) {
-        g_pre[g] = run;
-        run += (g_hi[g] - g_lo[g] + BM - 1) / BM;
-      }
-      if (lane == 63) g_pre[ng] = incl;
+    const int tile = tile_id;
+    const int MT = gl.pre[ng];
+    const int band = GM_BAND * sp.NBt;
+    const int sup = tile / band, within = tile % band;
+    const int first = sup * GM_BAND;
+    const int gsz = min(GM_BAND, MT - first);
+    const int mi = first + within % gsz;
+    const int nbi = within / gsz;
+    // group of M-tile mi: last g with pre[g] <= mi and a non-empty range
+    int lo = 0, hi = ng - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gl.pre[mid] <= mi) lo = mid; else hi = mid - 1;
     }
-    __syncthreads();
-    const int nb = (MODE == FWD1) ? (a.I + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-    NBt = nb;
-    total = g_pre[ng] * nb;
-    if constexpr (LIGHT) {
-      // light builds in use where at least half of the M-tiles are light (a
-      // group's last M-tile holding at most 64 rows): a few light tiles among
-      // full ones finish early, let some XCDs run ahead of the others and
-      // widen the stretch of operand panels the chip works on (HBM reads of
-      // the Pangu share's launches grew by 7-63% for no gain in time)
-      if (wave == 0) {
-        int lt = 0;
-        for (int g = lane; g < ng; g += 64) {
-          const int r = g_hi[g] - g_lo[g];
-          lt += (r > 0 && r - (r - 1) / BM * BM <= 64);
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 64);
-        if (lane == 0) s_next = lt;   // (s_next is free until the first epilogue)
-      }
-      __syncthreads();
-      light = 2 * s_next >= g_pre[ng];
-      __syncthreads();   // s_next is written again at the first epilogue
-    }
+    g = lo;
+    rows0 = gl.lo[g] + (mi - gl.pre[g]) * BM;
+    rows = min(BM, gl.hi[g] - rows0);
+    m0 = 0;
+    n0 = nbi * ((MODE == FWD1) ? BN / 2 : BN);
+    kdim = a.K;
   } else {
-    // stable order by descending row count: g_pre[rank] = g
-    for (int g = tid; g < ng; g += NT) {
-      const int c = g_hi[g] - g_lo[g];
-      int rank = 0;
-      for (int h = 0; h < ng; ++h) {
-        const int ch = g_hi[h] - g_lo[h];
-        rank += (ch > c) || (ch == c && h < g);
-      }
-      g_pre[rank] = g;
-    }
-    __syncthreads();
-    MBt = (a.M + BM - 1) / BM;
-    NBt = (a.N + BN - 1) / BN;
-    total = ng * MBt * NBt;
-    // work of a group = its tiles x max(1, K steps) (an empty group still
-    // owns tiles that must be written with zeros)
-    if (wave == 0) {
-      const int per = (ng + 63) / 64;
-      const int b0 = lane * per, b1 = min(ng, b0 + per);
-      auto work = [&](int p) {
-        const int g = g_pre[p];
-        return MBt * NBt * max(1, (g_hi[g] - g_lo[g] + BK - 1) / BK);
-      };
-      int s = 0;
-      for (int p = b0; p < b1; ++p) s += work(p);
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      int run = incl - s;
-      for (int p = b0; p < b1; ++p) {
-        g_kp[p] = run;
-        run += work(p);
-      }
-      if (lane == 63) g_kp[ng] = incl;
-    }
-    __syncthreads();
+    const int per = sp.MBt * sp.NBt;   // tiles of one group
+    const int p = tile_id / per, local = tile_id % per;
+    g = gl.ord[p];
+    const int band = GM_BAND * sp.NBt;
+    const int sup = local / band, within = local % band;
+    const int first = sup * GM_BAND;
+    const int gsz = min(GM_BAND, sp.MBt - first);
+    m0 = (first + within % gsz) * BM;
+    n0 = (within / gsz) * BN;
+    rows0 = gl.lo[g];
+    kdim = gl.hi[g] - gl.lo[g];
+  }
+  g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
+  rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
+  const bool sh = g >= a.G;
+  const bool gat = GATHER && !sh;   // routed tile of a gathering launch
+  const long long xg = a.dense ? (long long)g * a.x_gs * ES : 0;   // dense group bases
+  const int arows = a.kwrap > 0 ? a.kwrap : kdim;   // A rows a DW tile can touch
+
+  // ---- operand views
+  View va, vb;
+  if constexpr (MODE != DW) {
+    const void* xb = sh ? a.sX : (const void*)((const char*)a.X + xg);
+    if (gat)   // FWD1: the rows are gathered from the whole token matrix
+      va = make_view(a.X, (long long)a.gather_rows * a.ldx * ES, a.ldx, rows);
+    else
+      va = make_view((const char*)xb + (long long)rows0 * a.ldx * ES,
+                     (long long)rows * a.ldx * ES, a.ldx, rows);
+    const void* wb = sh ? a.sW : (const void*)((const char*)a.W + (long long)g * a.w_gs * ES);
+    const int wrows = (MODE == FWD1) ? 2 * a.I : (B_MN ? a.K : a.N);  // stored rows of W
+    const int wcols = B_MN ? a.N : a.K;
+    vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, a.N);
+  } else {
+    const void* pb = sh ? a.sX : (const void*)((const char*)a.X + xg);
+    const void* qb = sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)g * a.w_gs * ES : 0));
+    va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
+                   a.ldx, a.M);
+    if (gat)   // DW: Q's K rows are gathered from the whole token matrix
+      vb = make_view(a.W, (long long)a.gather_rows * a.ldw * ES, a.ldw, a.N);
+    else
+      vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES,
+                     (long long)kdim * a.ldw * ES, a.ldw, a.N);
   }
 
-  // ---- persistent loop over tiles.  Tiles are dealt in rounds of one per
-  // workgroup; in each round the workgroups of XCD x (workgroup i runs on XCD
-  // i % 8) take the round's x-th block of consecutive tiles, so an XCD's
-  // workgroups share operand panels in its L2 and the whole chip works on one
-  // compact stretch of tiles at a time (whose operands stay in the MALL).
-  // Without a workspace workgroup w of an XCD takes the w-th tile of each of
-  // its blocks; with one the XCD's workgroups draw its tiles in order from the
-  // XCD's counter, so a workgroup that starts late (its CU was still busy
-  // with another kernel) or drew short tiles just takes fewer or more.
-  const int nwg = gridDim.x;
-  const int bid = blockIdx.x;
-  const int nx = (nwg % 8 == 0) ? 8 : 1;
-  const int xcd = bid % nx, wpx = nwg / nx, wix = bid / nx;
-  const int per = MBt * NBt;             // DW: tiles of one group
-  // n-th tile of this XCD's sequence
-  auto tile_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
-  int* const ctr = a.cnt;   // [0, 8): per-XCD tile counters, [8]: finished workgroups
-  const bool dyn = ctr != nullptr;
-  int k = wix;              // index of this workgroup's tile inside the chunk
-  int grab = 0;             // thread 0: the counter value drawn at the start of this tile
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (bool first = true;; first = false) {
-    // every wave is done reading the ring (previous tile) and s_next holds
-    // the next tile; the previous tile's stores may still be draining --
-    // they overlap this tile's first copies (the copy waits below count them
-    // too, which only makes them wait longer)
+  const int KT = (kdim + BK - 1) / BK;   // K steps with data
+  uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
+  if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
+  else if (GATHER && MODE == FWD1 && gat)
+    kmajor_offsets_gather<T>(va, a.gather, rows0, rows, offa);
+  else kmajor_offsets<T, false>(va, m0, 0, offa);
+  if constexpr (GLOOP) {
+    // gathered Q: only the column part is fixed; the row part comes with
+    // each K step's indices (view with ld 0 gives column offsets)
+    View vc = vb;
+    if (gat) vc.ld = 0;
+    mnmajor_offsets<T>(vc, n0, offb);
+  } else if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
+  else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
+  const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
+  const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
+  const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
+  auto issue = [&](int kt) {
+    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    issue_op(va, st, offa, (kt % wrap_steps) * sa);
+    issue_op(vb, st + OPB, offb, kt * sb);
+  };
+  // copy j of K step kt (j < DMA_PER_OP: operand A, else B); a step past the
+  // last one copies through an empty descriptor, which moves no HBM bytes
+  // and only writes zeros into a stage nobody reads
+  const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
+  const uint32_t lds_w = lds_addr(smem) + (threadIdx.x >> 6) * DMA_PER_OP * 1024;
+  // (the A step index wraps for dW tiles that re-read a short operand;
+  // ka_next tracks kt % wrap_steps of the next step to issue)
+  int ka_next = 0;
+  auto issue1 = [&](int kt, int j) {
+    const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const bool live = kt < KT;
+    if (j < DMA_PER_OP)
+      dma16(live ? va.rs : rs_none, st + j * 1024, offa[j], ka_next * sa);
+    else
+      dma16(live ? vb.rs : rs_none, st + OPB + (j - DMA_PER_OP) * 1024, offb[j - DMA_PER_OP],
+            kt * sb);
+    if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
+  };
+  auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
+  // GLOOP: B copy j of a step covers K rows 8 wave + 2 j + (0, 1), lane l
+  // the row l / 32.  The indices of a wave's 8 rows of step kt are copied
+  // to its slot kt % 4 in the order 0 2 4 6 1 3 5 7, so a lane's four
+  // indices are one 16-byte read.
+  const int hrow = lane >> 5;
+  i32x4 rs_g = rs_none;
+  uint32_t goff = OOB;
+  if constexpr (GLOOP) {
+    if (gat)
+      rs_g = raw_rsrc((const char*)a.gather + (long long)rows0 * 4,
+                      clamp_bytes((long long)kdim * 4));
+    goff = lane < 8 ? (uint32_t)((8 * wave + 2 * (lane & 3) + (lane >> 2)) * 4) : OOB;
+  }
+  const uint32_t lds_g = lds_addr((const char*)g_idx) + (uint32_t)(wave * 4 * 256);
+  const uint32_t rowb = (uint32_t)(vb.ld * ES);
+  auto issue_idx = [&](int kt) {
+    dma4(kt < KT ? rs_g : rs_none, lds_g + (uint32_t)((kt & 3) * 256), goff, kt * BK * 4);
+  };
+  auto read_idx = [&](int kt) {
+    return *(const u32x4*)(g_idx + (wave * 4 + (kt & 3)) * 64 + 4 * hrow);
+  };
+  auto issue_b = [&](int kt, int j, const u32x4& iv) {
+    const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const int krow = kt * BK + 8 * wave + 2 * j + hrow;
+    const uint32_t vo =
+        gat ? ((krow < kdim && offb[j] != OOB) ? iv[j] * rowb + offb[j] : OOB) : offb[j];
+    dma16(kt < KT ? vb.rs : rs_none, st + OPB + j * 1024, vo, kt * sb);
+    if (j == DMA_PER_OP - 1 && ++ka_next == wrap_steps) ka_next = 0;
+  };
+
+  if (KT > 0) {
+    if constexpr (sizeof(T) == 2) {
+      // steps 0, 1 and 2 in flight (empty copies past the end), so the
+      // wait counts below hold for every K step
+      if constexpr (GLOOP) {
+        // indices of steps 0-2 first; then per step A, B and the indices
+        // of two steps on, in the order the loop keeps
+        issue_idx(0);
+        issue_idx(1);
+        issue_idx(2);
+        wait_vm<0>();
+        asm volatile("" ::: "memory");
+        const u32x4 iv[3] = {read_idx(0), read_idx(1), read_idx(2)};
+#pragma unroll
+        for (int kt = 0; kt < STAGES - 1; ++kt) {
+#pragma unroll
+          for (int j = 0; j < DMA_PER_OP; ++j) issue1(kt, j);
+#pragma unroll
+          for (int j = 0; j < DMA_PER_OP; ++j) issue_b(kt, j, iv[kt]);
+          if (kt >= 1) issue_idx(kt + 2);
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < STAGES - 1; ++kt)
+#pragma unroll
+          for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
+      }
+      wait_vm<2 * DMA_PER_STEP + 2 * GI>();
+    } else {
+      for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
+      if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
+      else if (KT == 2) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+    }
     __syncthreads();
-    if (!first) k = dyn ? s_next : k + wpx;
-    k = uniform(k);
-    const int tile_id = tile_of(k);
-    if (tile_id >= total) break;
-    // draw the tile after this one now: the atomic returns long before its
-    // value is read, at the epilogue's full wait
-    if (dyn && tid == 0)
-      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // ---- locate the tile
-    int g, m0, n0, rows0 = 0, rows = 0, kdim;
-    if constexpr (MODE != DW) {
-      const int tile = tile_id;
-      const int MT = g_pre[ng];
-      const int band = GM_BAND * NBt;
-      const int sup = tile / band, within = tile % band;
-      const int first = sup * GM_BAND;
-      const int gsz = min(GM_BAND, MT - first);
-      const int mi = first + within % gsz;
-      const int nbi = within / gsz;
-      // group of M-tile mi: last g with g_pre[g] <= mi and a non-empty range
-      int lo = 0, hi = ng - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (g_pre[mid] <= mi) lo = mid; else hi = mid - 1;
-      }
-      g = lo;
-      rows0 = g_lo[g] + (mi - g_pre[g]) * BM;
-      rows = min(BM, g_hi[g] - rows0);
-      m0 = 0;
-      n0 = nbi * ((MODE == FWD1) ? BN / 2 : BN);
-      kdim = a.K;
-    } else {
-      const int p = tile_id / per, local = tile_id % per;
-      g = g_pre[p];
-      const int band = GM_BAND * NBt;
-      const int sup = local / band, within = local % band;
-      const int first = sup * GM_BAND;
-      const int gsz = min(GM_BAND, MBt - first);
-      m0 = (first + within % gsz) * BM;
-      n0 = (within / gsz) * BN;
-      rows0 = g_lo[g];
-      kdim = g_hi[g] - g_lo[g];
-    }
-    g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
-    rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
-    const bool sh = g >= a.G;
-    const bool gat = GATHER && !sh;   // routed tile of a gathering launch
-    const long long xg = a.dense ? (long long)g * a.x_gs * ES : 0;   // dense group bases
-    const int arows = a.kwrap > 0 ? a.kwrap : kdim;   // A rows a DW tile can touch
-
-    // ---- operand views
-    View va, vb;
-    if constexpr (MODE != DW) {
-      const void* xb = sh ? a.sX : (const void*)((const char*)a.X + xg);
-      if (gat)   // FWD1: the rows are gathered from the whole token matrix
-        va = make_view(a.X, (long long)a.gather_rows * a.ldx * ES, a.ldx, rows);
-      else
-        va = make_view((const char*)xb + (long long)rows0 * a.ldx * ES,
-                       (long long)rows * a.ldx * ES, a.ldx, rows);
-      const void* wb = sh ? a.sW : (const void*)((const char*)a.W + (long long)g * a.w_gs * ES);
-      const int wrows = (MODE == FWD1) ? 2 * a.I : (B_MN ? a.K : a.N);  // stored rows of W
-      const int wcols = B_MN ? a.N : a.K;
-      vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, a.N);
-    } else {
-      const void* pb = sh ? a.sX : (const void*)((const char*)a.X + xg);
-      const void* qb = sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)g * a.w_gs * ES : 0));
-      va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
-                     a.ldx, a.M);
-      if (gat)   // DW: Q's K rows are gathered from the whole token matrix
-        vb = make_view(a.W, (long long)a.gather_rows * a.ldw * ES, a.ldw, a.N);
-      else
-        vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES,
-                       (long long)kdim * a.ldw * ES, a.ldw, a.N);
-    }
-
-    f32x16 acc[FM][FN];
+    if constexpr (sizeof(T) == 2) {
+      // two fragment sets in ping-pong.  Each half K step's 16 MFMAs carry
+      // the other work woven between them (pinned by scheduling barriers),
+      // so the matrix pipe never waits on a burst of LDS reads or copy
+      // issues: the first half loads the second half's fragments and issues
+      // the A copies of step kt+3; the second half (after the barrier)
+      // loads the first half fragments of step kt+1 and issues the B copies
+      // of step kt+3 (step kt+3's stage held step kt-1, whose last reads
+      // retired at the previous barrier; splitting a step's copies over two
+      // halves measured ~10% fewer cycles per step than issuing them
+      // together).  Steps past the end
+      // copy through the empty descriptor, so every step looks the same.
+      // LIGHT builds: the loop is built per count FA of this wave's A
+      // fragments that hold rows of the tile; in a tile of a group with few
+      // rows the upper fragments (and the lower waves) see padding only, so
+      // their MFMAs and A-fragment reads are left out (their accumulators
+      // stay zero and their rows are never stored).  Copies, waits and
+      // barriers are the same in every build, so the waves of a workgroup
+      // stay in step, and every output is the same bits as without.
+      auto kloop = [&](auto fa_c) {
+        constexpr int FA = decltype(fa_c)::value;
+        // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
+        auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
+        Frags<T, A_MN, B_MN> f0, f1;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int KT = (kdim + BK - 1) / BK;   // K steps with data
-    uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
-    if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
-    else if (GATHER && MODE == FWD1 && gat)
-      kmajor_offsets_gather<T>(va, a.gather, rows0, rows, offa);
-    else kmajor_offsets<T, false>(va, m0, 0, offa);
-    if constexpr (GLOOP) {
-      // gathered Q: only the column part is fixed; the row part comes with
-      // each K step's indices (view with ld 0 gives column offsets)
-      View vc = vb;
-      if (gat) vc.ld = 0;
-      mnmajor_offsets<T>(vc, n0, offb);
-    } else if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
-    else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
-    const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
-    const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
-    const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
-    auto issue = [&](int kt) {
-      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-      issue_op(va, st, offa, (kt % wrap_steps) * sa);
-      issue_op(vb, st + OPB, offb, kt * sb);
-    };
-    // copy j of K step kt (j < DMA_PER_OP: operand A, else B); a step past the
-    // last one copies through an empty descriptor, which moves no HBM bytes
-    // and only writes zeros into a stage nobody reads
-    const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
-    const uint32_t lds_w = lds_addr(smem) + (threadIdx.x >> 6) * DMA_PER_OP * 1024;
-    // (the A step index wraps for dW tiles that re-read a short operand;
-    // ka_next tracks kt % wrap_steps of the next step to issue)
-    int ka_next = 0;
-    auto issue1 = [&](int kt, int j) {
-      const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
-      const bool live = kt < KT;
-      if (j < DMA_PER_OP)
-        dma16(live ? va.rs : rs_none, st + j * 1024, offa[j], ka_next * sa);
-      else
-        dma16(live ? vb.rs : rs_none, st + OPB + (j - DMA_PER_OP) * 1024, offb[j - DMA_PER_OP],
-              kt * sb);
-      if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
-    };
-    auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
-    // GLOOP: B copy j of a step covers K rows 8 wave + 2 j + (0, 1), lane l
-    // the row l / 32.  The indices of a wave's 8 rows of step kt are copied
-    // to its slot kt % 4 in the order 0 2 4 6 1 3 5 7, so a lane's four
-    // indices are one 16-byte read.
-    const int hrow = lane >> 5;
-    i32x4 rs_g = rs_none;
-    uint32_t goff = OOB;
-    if constexpr (GLOOP) {
-      if (gat)
-        rs_g = raw_rsrc((const char*)a.gather + (long long)rows0 * 4,
-                        clamp_bytes((long long)kdim * 4));
-      goff = lane < 8 ? (uint32_t)((8 * wave + 2 * (lane & 3) + (lane >> 2)) * 4) : OOB;
-    }
-    const uint32_t lds_g = lds_addr((const char*)g_idx) + (uint32_t)(wave * 4 * 256);
-    const uint32_t rowb = (uint32_t)(vb.ld * ES);
-    auto issue_idx = [&](int kt) {
-      dma4(kt < KT ? rs_g : rs_none, lds_g + (uint32_t)((kt & 3) * 256), goff, kt * BK * 4);
-    };
-    auto read_idx = [&](int kt) {
-      return *(const u32x4*)(g_idx + (wave * 4 + (kt & 3)) * 64 + 4 * hrow);
-    };
-    auto issue_b = [&](int kt, int j, const u32x4& iv) {
-      const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
-      const int krow = kt * BK + 8 * wave + 2 * j + hrow;
-      const uint32_t vo =
-          gat ? ((krow < kdim && offb[j] != OOB) ? iv[j] * rowb + offb[j] : OOB) : offb[j];
-      dma16(kt < KT ? vb.rs : rs_none, st + OPB + j * 1024, vo, kt * sb);
-      if (j == DMA_PER_OP - 1 && ++ka_next == wrap_steps) ka_next = 0;
-    };
-
-    if (KT > 0) {
-      if constexpr (sizeof(T) == 2) {
-        // steps 0, 1 and 2 in flight (empty copies past the end), so the
-        // wait counts below hold for every K step
-        if constexpr (GLOOP) {
-          // indices of steps 0-2 first; then per step A, B and the indices
-          // of two steps on, in the order the loop keeps
-          issue_idx(0);
-          issue_idx(1);
-          issue_idx(2);
-          wait_vm<0>();
-          asm volatile("" ::: "memory");
-          const u32x4 iv[3] = {read_idx(0), read_idx(1), read_idx(2)};
-#pragma unroll
-          for (int kt = 0; kt < STAGES - 1; ++kt) {
-#pragma unroll
-            for (int j = 0; j < DMA_PER_OP; ++j) issue1(kt, j);
-#pragma unroll
-            for (int j = 0; j < DMA_PER_OP; ++j) issue_b(kt, j, iv[kt]);
-            if (kt >= 1) issue_idx(kt + 2);
-          }
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < STAGES - 1; ++kt)
-#pragma unroll
-            for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
-        }
-        wait_vm<2 * DMA_PER_STEP + 2 * GI>();
-      } else {
-        for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
-        if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
-        else if (KT == 2) wait_vm<DMA_PER_STEP>();
-        else wait_vm<0>();
-      }
-      __syncthreads();
-      if constexpr (sizeof(T) == 2) {
-        // two fragment sets in ping-pong.  Each half K step's 16 MFMAs carry
-        // the other work woven between them (pinned by scheduling barriers),
-        // so the matrix pipe never waits on a burst of LDS reads or copy
-        // issues: the first half loads the second half's fragments and issues
-        // the A copies of step kt+3; the second half (after the barrier)
-        // loads the first half fragments of step kt+1 and issues the B copies
-        // of step kt+3 (step kt+3's stage held step kt-1, whose last reads
-        // retired at the previous barrier; splitting a step's copies over two
-        // halves measured ~10% fewer cycles per step than issuing them
-        // together).  Steps past the end
-        // copy through the empty descriptor, so every step looks the same.
-        // LIGHT builds: the loop is built per count FA of this wave's A
-        // fragments that hold rows of the tile; in a tile of a group with few
-        // rows the upper fragments (and the lower waves) see padding only, so
-        // their MFMAs and A-fragment reads are left out (their accumulators
-        // stay zero and their rows are never stored).  Copies, waits and
-        // barriers are the same in every build, so the waves of a workgroup
-        // stay in step, and every output is the same bits as without.
-        auto kloop = [&](auto fa_c) {
-          constexpr int FA = decltype(fa_c)::value;
-          // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
-          auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
-          Frags<T, A_MN, B_MN> f0, f1;
-#pragma unroll
-          for (int q = 0; q < FM + FN; ++q)
-            if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
-          for (int kt = 0; kt < KT; ++kt) {
-            const char* cs = stage(kt);
-            const char* ns = stage(kt + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                if (i < FA) acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) {
-                  if (need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-                } else if (q - (FM + FN) < DMA_PER_OP) {
-                  issue1(kt + STAGES - 1, q - (FM + FN));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                if (i < FA) acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) {
-                  if (need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-                } else if (q - (FM + FN) < DMA_PER_OP) {
-                  issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-          }
-        };
-        if constexpr (LIGHT) {
-          const int rw = rows - wm * WTM;             // rows of the tile in this wave's half
-          const int fa = light ? uniform(rw <= 0 ? 0 : min(FM, (rw + 31) / 32)) : FM;
-          switch (fa) {
-            case 0: kloop(std::integral_constant<int, 0>{}); break;
-            case 1: kloop(std::integral_constant<int, 1>{}); break;
-            case 2: kloop(std::integral_constant<int, 2>{}); break;
-            case 3: kloop(std::integral_constant<int, 3>{}); break;
-            default: kloop(std::integral_constant<int, FM>{}); break;
-          }
-        } else {
-          Frags<T, A_MN, B_MN> f0, f1;
-          f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
-          for (int kt = 0; kt < KT; ++kt) {
-            const char* cs = stage(kt);
-            const char* ns = stage(kt + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-                else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            // K step kt+1 has landed once at most the copies issued after it
-            // (step kt+2, and step kt+3's A copies) are outstanding; the
-            // barrier extends that to all waves and retires every read of the
-            // stage refilled next
-            // (GLOOP: also step kt+3's indices, issued right after step
-            // kt+1's B copies, and one index copy more per step since)
-            wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
-            __syncthreads();
-            u32x4 ivn;
-            if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int q = i * FN + j;
-                acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-                else if (q - (FM + FN) < DMA_PER_OP) {
-                  if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
-                  else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-                } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
-                  issue_idx(kt + STAGES + 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-          }
-        }
-      } else {
-        Frags<T, A_MN, B_MN> cur, nxt;
-        cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
+        for (int q = 0; q < FM + FN; ++q)
+          if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
         for (int kt = 0; kt < KT; ++kt) {
+          const char* cs = stage(kt);
+          const char* ns = stage(kt + 1);
 #pragma unroll
-          for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
-            if (ks == Cfg<T>::KS - 1) {
-              if (kt + 1 < KT) {
-                if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
-                else wait_vm<0>();
-                __syncthreads();
-                if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-                nxt.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              if (i < FA) acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) {
+                if (need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+              } else if (q - (FM + FN) < DMA_PER_OP) {
+                issue1(kt + STAGES - 1, q - (FM + FN));
               }
-            } else {
-              nxt.load(stage(kt), stage(kt) + OPB, wm, wn, ks + 1);
+              __builtin_amdgcn_sched_barrier(0);
             }
-            cur.mma(acc);
-            cur = nxt;
+          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              if (i < FA) acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) {
+                if (need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+              } else if (q - (FM + FN) < DMA_PER_OP) {
+                issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+      };
+      if constexpr (LIGHT) {
+        const int rw = rows - wm * WTM;             // rows of the tile in this wave's half
+        const int fa = sp.light ? uniform(rw <= 0 ? 0 : min(FM, (rw + 31) / 32)) : FM;
+        switch (fa) {
+          case 0: kloop(std::integral_constant<int, 0>{}); break;
+          case 1: kloop(std::integral_constant<int, 1>{}); break;
+          case 2: kloop(std::integral_constant<int, 2>{}); break;
+          case 3: kloop(std::integral_constant<int, 3>{}); break;
+          default: kloop(std::integral_constant<int, FM>{}); break;
+        }
+      } else {
+        Frags<T, A_MN, B_MN> f0, f1;
+        f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
+        for (int kt = 0; kt < KT; ++kt) {
+          const char* cs = stage(kt);
+          const char* ns = stage(kt + 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          // K step kt+1 has landed once at most the copies issued after it
+          // (step kt+2, and step kt+3's A copies) are outstanding; the
+          // barrier extends that to all waves and retires every read of the
+          // stage refilled next
+          // (GLOOP: also step kt+3's indices, issued right after step
+          // kt+1's B copies, and one index copy more per step since)
+          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+          __syncthreads();
+          u32x4 ivn;
+          if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int q = i * FN + j;
+              acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+              else if (q - (FM + FN) < DMA_PER_OP) {
+                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
+                else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
+              } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
+                issue_idx(kt + STAGES + 1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+      }
+    } else {
+      Frags<T, A_MN, B_MN> cur, nxt;
+      cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int ks = 0; ks < Cfg<T>::KS; ++ks) {
+          if (ks == Cfg<T>::KS - 1) {
+            if (kt + 1 < KT) {
+              if (kt + 2 < KT) wait_vm<DMA_PER_STEP>();
+              else wait_vm<0>();
+              __syncthreads();
+              if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+              nxt.load(stage(kt + 1), stage(kt + 1) + OPB, wm, wn, 0);
+            }
+          } else {
+            nxt.load(stage(kt), stage(kt) + OPB, wm, wn, ks + 1);
           }
+          cur.mma(acc);
+          cur = nxt;
         }
       }
     }
+  }
 
-    // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
-    // every HBM access is a 16-byte row chunk.  Slice s holds fragments 2s and
-    // 2s+1 of every wave (FWD1: s = 0 gate, s = 1 up columns).
-    // a per-tile copy of the thread index: the epilogue's address arithmetic
-    // then belongs to this tile and is not kept live (and spilled) across
-    // the persistent loop as an invariant
-    int etid = threadIdx.x;
-    asm volatile("" : "+v"(etid));
-    const int elane = etid & 63;
-    wait_vm<0>();      // the empty copies past the last step (and the draw) have landed
-    if (dyn && tid == 0) s_next = wpx + grab;   // read after the next loop-top barrier
-    __syncthreads();   // every wave is done with the ring
-    float* ep = (float*)smem;
-    auto put = [&](auto fn0c, auto&& value) {
-      // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
-      // (fn0 is a compile-time constant so the accumulators stay in registers);
-      // 16-byte granule g of row m sits at g ^ (m % 32), so the 32 rows of a
-      // store and the 16 chunks of a row read all hit distinct banks
-      constexpr int slice_fn0 = decltype(fn0c)::value;
+  // ---- epilogue: the tile leaves through LDS in 256 x 128 fp32 slices, so
+  // every HBM access is a 16-byte row chunk.  Slice s holds fragments 2s and
+  // 2s+1 of every wave (FWD1: s = 0 gate, s = 1 up columns).
+  // a per-tile copy of the thread index: the epilogue's address arithmetic
+  // then belongs to this tile and is not kept live (and spilled) across
+  // the persistent loop as an invariant
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int elane = etid & 63;
+  wait_vm<0>();      // the empty copies past the last step (and the draw) have landed
+  drained();   // the scheduler's draw has returned: publish the next tile
+  __syncthreads();   // every wave is done with the ring
+  float* ep = (float*)smem;
+  auto put = [&](auto fn0c, auto&& value) {
+    // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
+    // (fn0 is a compile-time constant so the accumulators stay in registers);
+    // 16-byte granule g of row m sits at g ^ (m % 32), so the 32 rows of a
+    // store and the 16 chunks of a row read all hit distinct banks
+    constexpr int slice_fn0 = decltype(fn0c)::value;
+    const int m = elane & 31;
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int row = wm * WTM + f * 32 + m;
+          const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
+          f32x4 v;
+          v.x = value(f, slice_fn0 + j, rq * 4 + 0);
+          v.y = value(f, slice_fn0 + j, rq * 4 + 1);
+          v.z = value(f, slice_fn0 + j, rq * 4 + 2);
+          v.w = value(f, slice_fn0 + j, rq * 4 + 3);
+          *(f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2)) = v;
+        }
+    __syncthreads();
+  };
+  auto take = [&](auto&& consume) {
+    // 256 rows x 16 chunks of 8 columns, 16 per thread
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * NT + etid;
+      const int row = idx >> 4, cc = (idx & 15) * 8;
+      const int sw = row & 31;
+      float v[8];
+      const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
+      const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      consume(row, cc, v);
+    }
+    __syncthreads();
+  };
+  auto acc_of = [&](int f, int fn, int r) { return acc[f][fn][r]; };
+
+  // slice sl of the finished tile -> consume(row, c, v[8])
+  auto emit = [&](auto slc, auto&& consume) {
+    constexpr int sl = decltype(slc)::value;
+    put(std::integral_constant<int, 2 * sl>{}, acc_of);
+    take(consume);
+  };
+
+  // 8 values at element elem of an output (dropped unless ok)
+  // every output leaves with the streaming cache policy: measured ~1.5%
+  // faster over the layer step than plain stores (also with yp or act kept
+  // cached for the kernel that reads them next)
+  auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, const float* v) {
+    if constexpr (sizeof(T) == 2) {
+      buf_store16_nt(rs, ok ? elem * 2u : DROP, pack16(v, T()));
+    } else {
+      buf_store16_nt(rs, ok ? elem * 4u : DROP, pack16(v, T()));
+      buf_store16_nt(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
+    }
+  };
+  // 8 values at element elem of an operand (zeros unless ok)
+  auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, float* v) {
+    if constexpr (sizeof(T) == 2) {
+      unpack16(buf_load16(rs, ok ? elem * 2u : OOB), v, T());
+    } else {
+      unpack16(buf_load16(rs, ok ? elem * 4u : OOB), v, T());
+      unpack16(buf_load16(rs, ok ? elem * 4u + 16u : OOB), v + 4, T());
+    }
+  };
+  if constexpr (MODE == FWD1) {
+    // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + elane%32,
+    // fragments 2,3 the matching up columns; LDS column c is i = i0 + c
+    void* hb = sh ? a.sC : a.C;
+    void* ab = sh ? a.sC2 : a.C2;
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc((char*)hb + (long long)rows0 * a.ldc * ES,
+                                                out_bytes((long long)rows * a.ldc * ES));
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc((char*)ab + (long long)rows0 * a.ldc2 * ES,
+                                                out_bytes((long long)rows * a.ldc2 * ES));
+    auto store_gate = [&](int row, int c, const float* v) {
+      store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + n0 + c), v);
+    };
+    auto store_up = [&](int row, int c, const float* v) {
+      store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
+    };
+    auto store_act = [&](int row, int c, const float* v) {
+      store8(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
+    };
+    // gate slice out; then act = silu(g) * u replaces it in LDS (each
+    // elane rewrites the very words it put, so no barrier in between and
+    // the gate accumulators are dead once the slice is staged); up last
+    put(std::integral_constant<int, 0>{}, acc_of);
+    take(store_gate);
+    {
       const int m = elane & 31;
 #pragma unroll
       for (int f = 0; f < FM; ++f)
@@ -878,225 +937,193 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
           for (int rq = 0; rq < 4; ++rq) {
             const int row = wm * WTM + f * 32 + m;
             const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
-            f32x4 v;
-            v.x = value(f, slice_fn0 + j, rq * 4 + 0);
-            v.y = value(f, slice_fn0 + j, rq * 4 + 1);
-            v.z = value(f, slice_fn0 + j, rq * 4 + 2);
-            v.w = value(f, slice_fn0 + j, rq * 4 + 3);
-            *(f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2)) = v;
+            f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
+            f32x4 v = *pp;
+            const f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
+                             acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
+            v.x = swiglu_act<T>(v.x, u.x);
+            v.y = swiglu_act<T>(v.y, u.y);
+            v.z = swiglu_act<T>(v.z, u.z);
+            v.w = swiglu_act<T>(v.w, u.w);
+            *pp = v;
           }
       __syncthreads();
-    };
-    auto take = [&](auto&& consume) {
-      // 256 rows x 16 chunks of 8 columns, 16 per thread
-#pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int idx = it * NT + etid;
-        const int row = idx >> 4, cc = (idx & 15) * 8;
-        const int sw = row & 31;
-        float v[8];
-        const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
-        const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-        consume(row, cc, v);
-      }
-      __syncthreads();
-    };
-    auto acc_of = [&](int f, int fn, int r) { return acc[f][fn][r]; };
-
-    // slice sl of the finished tile -> consume(row, c, v[8])
-    auto emit = [&](auto slc, auto&& consume) {
-      constexpr int sl = decltype(slc)::value;
-      put(std::integral_constant<int, 2 * sl>{}, acc_of);
-      take(consume);
-    };
-
-    // 8 values at element elem of an output (dropped unless ok)
-    // every output leaves with the streaming cache policy: measured ~1.5%
-    // faster over the layer step than plain stores (also with yp or act kept
-    // cached for the kernel that reads them next)
-    auto store8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, const float* v) {
-      if constexpr (sizeof(T) == 2) {
-        buf_store16_nt(rs, ok ? elem * 2u : DROP, pack16(v, T()));
-      } else {
-        buf_store16_nt(rs, ok ? elem * 4u : DROP, pack16(v, T()));
-        buf_store16_nt(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
-      }
-    };
-    // 8 values at element elem of an operand (zeros unless ok)
-    auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, float* v) {
-      if constexpr (sizeof(T) == 2) {
-        unpack16(buf_load16(rs, ok ? elem * 2u : OOB), v, T());
-      } else {
-        unpack16(buf_load16(rs, ok ? elem * 4u : OOB), v, T());
-        unpack16(buf_load16(rs, ok ? elem * 4u + 16u : OOB), v + 4, T());
-      }
-    };
-    if constexpr (MODE == FWD1) {
-      // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + elane%32,
-      // fragments 2,3 the matching up columns; LDS column c is i = i0 + c
-      void* hb = sh ? a.sC : a.C;
-      void* ab = sh ? a.sC2 : a.C2;
-      const __amdgpu_buffer_rsrc_t hr = make_rsrc((char*)hb + (long long)rows0 * a.ldc * ES,
-                                                  out_bytes((long long)rows * a.ldc * ES));
-      const __amdgpu_buffer_rsrc_t ar = make_rsrc((char*)ab + (long long)rows0 * a.ldc2 * ES,
-                                                  out_bytes((long long)rows * a.ldc2 * ES));
-      auto store_gate = [&](int row, int c, const float* v) {
-        store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + n0 + c), v);
-      };
-      auto store_up = [&](int row, int c, const float* v) {
-        store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
-      };
-      auto store_act = [&](int row, int c, const float* v) {
-        store8(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
-      };
-      // gate slice out; then act = silu(g) * u replaces it in LDS (each
-      // elane rewrites the very words it put, so no barrier in between and
-      // the gate accumulators are dead once the slice is staged); up last
-      put(std::integral_constant<int, 0>{}, acc_of);
-      take(store_gate);
-      {
-        const int m = elane & 31;
+    }
+    take(store_act);
+    put(std::integral_constant<int, 2>{}, acc_of);
+    take(store_up);
+  } else {
+    // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
+    auto slice = [&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      if constexpr (MODE == DX1) {
+        const void* hb = sh ? a.sAux : a.aux;
+        void* db = sh ? a.sC : a.C;
+        const __amdgpu_buffer_rsrc_t hr = make_rsrc(
+            (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
+        const __amdgpu_buffer_rsrc_t dr = make_rsrc(
+            (char*)db + (long long)rows0 * a.ldc * ES, out_bytes((long long)rows * a.ldc * ES));
+        // d(act) -> d(gate), d(up) of act = silu(gate) * up
+        auto bwd8 = [&](bool ok, int row, int i, const float* d, const float* gv,
+                        const float* uv) {
+          float dg[8], du[8];
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const int row = wm * WTM + f * 32 + m;
-              const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
-              f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
-              f32x4 v = *pp;
-              const f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
-                               acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
-              v.x = swiglu_act<T>(v.x, u.x);
-              v.y = swiglu_act<T>(v.y, u.y);
-              v.z = swiglu_act<T>(v.z, u.z);
-              v.w = swiglu_act<T>(v.w, u.w);
-              *pp = v;
-            }
-        __syncthreads();
-      }
-      take(store_act);
-      put(std::integral_constant<int, 2>{}, acc_of);
-      take(store_up);
-    } else {
-      // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
-      auto slice = [&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        if constexpr (MODE == DX1) {
-          const void* hb = sh ? a.sAux : a.aux;
-          void* db = sh ? a.sC : a.C;
-          const __amdgpu_buffer_rsrc_t hr = make_rsrc(
-              (const char*)hb + (long long)rows0 * a.ldaux * ES, clamp_bytes((long long)rows * a.ldaux * ES));
-          const __amdgpu_buffer_rsrc_t dr = make_rsrc(
-              (char*)db + (long long)rows0 * a.ldc * ES, out_bytes((long long)rows * a.ldc * ES));
-          // d(act) -> d(gate), d(up) of act = silu(gate) * up
-          auto bwd8 = [&](bool ok, int row, int i, const float* d, const float* gv,
-                          const float* uv) {
-            float dg[8], du[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float sg = sigmoidf_(gv[e]);
-              dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
-              du[e] = d[e] * gv[e] * sg;
-            }
-            store8(dr, ok, (uint32_t)(row * a.ldc + i), dg);
-            store8(dr, ok, (uint32_t)(row * a.ldc + a.I + i), du);
+          for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoidf_(gv[e]);
+            dg[e] = d[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+            du[e] = d[e] * gv[e] * sg;
+          }
+          store8(dr, ok, (uint32_t)(row * a.ldc + i), dg);
+          store8(dr, ok, (uint32_t)(row * a.ldc + a.I + i), du);
+        };
+        if (sizeof(T) == 2) {
+          // bf16: the slice's gate/up chunks (16 per thread) are
+          // requested before the accumulators are staged, so their latency
+          // hides behind the LDS round trip instead of serializing with the
+          // stores (a load may not pass an earlier store to a buffer that
+          // could alias).  LEAN builds hold 8 chunks at a time (the second
+          // half is requested after the first half's stores), which keeps a
+          // kernel that also holds another product's code within the
+          // register file
+          constexpr int PF = LEAN ? 8 : 16;
+          u32x4 graw[PF], uraw[PF];
+          auto fetch = [&](int it) {
+            const int idx = it * NT + etid;
+            const int row = idx >> 4, cc = (idx & 15) * 8;
+            const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+            const bool ok = row < rows && i < a.I;
+            graw[it % PF] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + i) * 2u : OOB);
+            uraw[it % PF] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + a.I + i) * 2u : OOB);
           };
-          if (sizeof(T) == 2) {
-            // bf16: the slice's gate/up chunks (16 per thread) are
-            // requested before the accumulators are staged, so their latency
-            // hides behind the LDS round trip instead of serializing with the
-            // stores (a load may not pass an earlier store to a buffer that
-            // could alias)
-            u32x4 graw[16], uraw[16];
-            auto fetch = [&](int it) {
-              const int idx = it * NT + etid;
-              const int row = idx >> 4, cc = (idx & 15) * 8;
-              const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
-              const bool ok = row < rows && i < a.I;
-              graw[it] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + i) * 2u : OOB);
-              uraw[it] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + a.I + i) * 2u : OOB);
-            };
-            auto finish = [&](int it) {
-              const int idx = it * NT + etid;
-              const int row = idx >> 4, cc = (idx & 15) * 8;
-              const int sw = row & 31;
-              const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
-              const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
-              const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-              const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
-              float gv[8], uv[8];
-              unpack16(graw[it], gv, T());
-              unpack16(uraw[it], uv, T());
-              bwd8(row < rows && i < a.I, row, i, d, gv, uv);
-            };
-            // first half requested before the staging, second half after it
-            // (ahead of the first half's stores)
+          auto finish = [&](int it) {
+            const int idx = it * NT + etid;
+            const int row = idx >> 4, cc = (idx & 15) * 8;
+            const int sw = row & 31;
+            const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
+            const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
+            const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+            float gv[8], uv[8];
+            unpack16(graw[it % PF], gv, T());
+            unpack16(uraw[it % PF], uv, T());
+            bwd8(row < rows && i < a.I, row, i, d, gv, uv);
+          };
+          // first half requested before the staging, second half after it
+          // (ahead of the first half's stores; LEAN: after them)
 #pragma unroll
-            for (int it = 0; it < 8; ++it) fetch(it);
-            put(std::integral_constant<int, 2 * h>{}, acc_of);
+          for (int it = 0; it < 8; ++it) fetch(it);
+          put(std::integral_constant<int, 2 * h>{}, acc_of);
+          if constexpr (LEAN) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it) finish(it);
+#pragma unroll
+            for (int it = 8; it < 16; ++it) fetch(it);
+#pragma unroll
+            for (int it = 8; it < 16; ++it) finish(it);
+          } else {
 #pragma unroll
             for (int it = 8; it < 16; ++it) fetch(it);
 #pragma unroll
             for (int it = 0; it < 16; ++it) finish(it);
-            __syncthreads();
-          } else {
-            emit(hc, [&](int row, int c, const float* d) {
-              const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
-              const bool ok = row < rows && i < a.I;
-              float gv[8], uv[8];
-              load8(hr, ok, (uint32_t)(row * a.ldaux + i), gv);
-              load8(hr, ok, (uint32_t)(row * a.ldaux + a.I + i), uv);
-              bwd8(ok, row, i, d, gv, uv);
-            });
           }
+          __syncthreads();
         } else {
-          // plain store: FWD2 / DX2 rows of C, or DW: dW[g] (M x N)
-          void* cb;
-          long long cbytes;
-          int lim_m;
-          const int OS = a.out_f32 ? 4 : ES;   // bytes per output element
-          if constexpr (MODE == DW) {
-            cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * OS);
-            cbytes = (long long)a.M * a.ldc * OS;
-            lim_m = a.M;
-          } else {
-            cb = (char*)(sh ? a.sC : a.C) + (a.dense ? (long long)g * a.c_gs * OS : 0) +
-                 (long long)rows0 * a.ldc * OS;
-            cbytes = (long long)rows * a.ldc * OS;
-            lim_m = rows;
-          }
-          const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, out_bytes(cbytes));
-          // (the output type is chosen outside the loop, which then
-          // unrolls into batches of LDS reads and stores)
-          auto place = [&](int row, int c, bool& ok) {
-            const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
-            const int m = m0 + row;
-            ok = m < lim_m && n < a.N;
-            return (uint32_t)(m * a.ldc + n);
-          };
-          if (a.out_f32) {
-            emit(hc, [&](int row, int c, const float* v) {
-              bool ok;
-              const uint32_t e = place(row, c, ok);
-              buf_store16_nt(cr, ok ? e * 4u : DROP, pack16(v, 0.0f));
-              buf_store16_nt(cr, ok ? e * 4u + 16u : DROP, pack16(v + 4, 0.0f));
-            });
-          } else {
-            emit(hc, [&](int row, int c, const float* v) {
-              bool ok;
-              const uint32_t e = place(row, c, ok);
-              store8(cr, ok, e, v);
-            });
-          }
+          emit(hc, [&](int row, int c, const float* d) {
+            const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+            const bool ok = row < rows && i < a.I;
+            float gv[8], uv[8];
+            load8(hr, ok, (uint32_t)(row * a.ldaux + i), gv);
+            load8(hr, ok, (uint32_t)(row * a.ldaux + a.I + i), uv);
+            bwd8(ok, row, i, d, gv, uv);
+          });
         }
-      };
-      slice(std::integral_constant<int, 0>{});
-      slice(std::integral_constant<int, 1>{});
-    }
+      } else {
+        // plain store: FWD2 / DX2 rows of C, or DW: dW[g] (M x N)
+        void* cb;
+        long long cbytes;
+        int lim_m;
+        const int OS = a.out_f32 ? 4 : ES;   // bytes per output element
+        if constexpr (MODE == DW) {
+          cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * OS);
+          cbytes = (long long)a.M * a.ldc * OS;
+          lim_m = a.M;
+        } else {
+          cb = (char*)(sh ? a.sC : a.C) + (a.dense ? (long long)g * a.c_gs * OS : 0) +
+               (long long)rows0 * a.ldc * OS;
+          cbytes = (long long)rows * a.ldc * OS;
+          lim_m = rows;
+        }
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, out_bytes(cbytes));
+        // (the output type is chosen outside the loop, which then
+        // unrolls into batches of LDS reads and stores)
+        auto place = [&](int row, int c, bool& ok) {
+          const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+          const int m = m0 + row;
+          ok = m < lim_m && n < a.N;
+          return (uint32_t)(m * a.ldc + n);
+        };
+        if (a.out_f32) {
+          emit(hc, [&](int row, int c, const float* v) {
+            bool ok;
+            const uint32_t e = place(row, c, ok);
+            buf_store16_nt(cr, ok ? e * 4u : DROP, pack16(v, 0.0f));
+            buf_store16_nt(cr, ok ? e * 4u + 16u : DROP, pack16(v + 4, 0.0f));
+          });
+        } else {
+          emit(hc, [&](int row, int c, const float* v) {
+            bool ok;
+            const uint32_t e = place(row, c, ok);
+            store8(cr, ok, e, v);
+          });
+        }
+      }
+    };
+    slice(std::integral_constant<int, 0>{});
+    slice(std::integral_constant<int, 1>{});
+  }
+}
+
+// ---------------------------------------------------------------- the kernels
+// Persistent tile loop.  Tiles are dealt in rounds of one per workgroup; in
+// each round the workgroups of XCD x (workgroup i runs on XCD i % 8) take the
+// round's x-th block of consecutive tiles, so an XCD's workgroups share
+// operand panels in its L2 and the whole chip works on one compact stretch of
+// tiles at a time (whose operands stay in the MALL).  Without a workspace
+// workgroup w of an XCD takes the w-th tile of each of its blocks; with one
+// the XCD's workgroups draw its tiles in order from the XCD's counter, so a
+// workgroup that starts late (its CU was still busy with another kernel) or
+// drew short tiles just takes fewer or more.  body(n, drained) runs the n-th
+// tile of the launch's sequence of total tiles.
+template <typename Body>
+__device__ __forceinline__ void persistent_loop(int* ctr, int total, int* s_next, Body&& body) {
+  const int tid = threadIdx.x;
+  const int nwg = gridDim.x;
+  const int bid = blockIdx.x;
+  const int nx = (nwg % 8 == 0) ? 8 : 1;
+  const int xcd = bid % nx, wpx = nwg / nx, wix = bid / nx;
+  // n-th tile of this XCD's sequence
+  auto tile_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
+  // ctr: [0, 8) per-XCD tile counters, [8] finished workgroups (NULL: static)
+  const bool dyn = ctr != nullptr;
+  int k = wix;              // index of this workgroup's tile in the XCD's sequence
+  int grab = 0;             // thread 0: the counter value drawn at the start of this tile
+  for (bool first = true;; first = false) {
+    // every wave is done reading the ring (previous tile) and s_next holds
+    // the next tile; the previous tile's stores may still be draining --
+    // they overlap this tile's first copies (the copy waits count them
+    // too, which only makes them wait longer)
+    __syncthreads();
+    if (!first) k = dyn ? *s_next : k + wpx;
+    k = uniform(k);
+    const int n = tile_of(k);
+    if (n >= total) break;
+    // draw the tile after this one now: the atomic returns long before its
+    // value is read, at the epilogue's full wait
+    if (dyn && tid == 0)
+      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    body(n, [&]() {
+      if (dyn && tid == 0) *s_next = wpx + grab;   // read after the next loop-top barrier
+    });
   }
   // every draw of this workgroup has returned (the last one ended the loop);
   // the last workgroup to finish returns the counters to zero for the next call
@@ -1106,6 +1133,56 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
       for (int i = 0; i <= 8; ++i)
         __hip_atomic_store(ctr + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
+__global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
+  constexpr bool GLOOP = GATHER && MODE == DW;
+  __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
+  __shared__ GroupLds gl;
+  __shared__ int s_next;
+  // GLOOP: [wave][step % 4][64] row indices (lanes 0-7 of each copy carry them)
+  __shared__ __attribute__((aligned(16))) int g_idx[GLOOP ? (NT / 64) * 4 * 64 : 4];
+  const int ng = a.G + a.shared;
+  load_groups(a, gl);
+  if constexpr (MODE != DW) tile_prefix(ng, gl);
+  else group_order(ng, gl);
+  const Space sp = tile_space<MODE, LIGHT>(a, gl, &s_next);
+  persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained) {
+    run_tile<T, MODE, GATHER, LIGHT, false>(a, gl, sp, n, smem, g_idx, drained);
+  });
+}
+
+// Two independent products of one call in one persistent launch (a row-tiled
+// product and a weight-gradient product on the same group window), so that
+// neither ends in a partial round of its own: the gradient tiles of groups
+// whose K (rows) is at least the row-tiled product's K run first, then the
+// row-tiled product, then the remaining (short) gradient tiles, which fill
+// the last round.
+template <typename T, int M1, int M2>
+__global__ __launch_bounds__(NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2) {
+  static_assert(M1 != DW && M2 == DW, "a row-tiled product and a weight-gradient product");
+  __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
+  __shared__ GroupLds gl;
+  __shared__ int s_next;
+  __shared__ int g_idx[4];
+  const int ng = a1.G + a1.shared;
+  load_groups(a1, gl);
+  tile_prefix(ng, gl);
+  group_order(ng, gl);
+  const Space s1 = tile_space<M1, false>(a1, gl, &s_next);
+  const Space s2 = tile_space<M2, false>(a2, gl, &s_next);
+  // leading gradient groups: K (rows) at least the row-tiled product's K
+  int lead = 0;
+  while (lead < ng && gl.hi[gl.ord[lead]] - gl.lo[gl.ord[lead]] >= a1.K) ++lead;
+  const int splitA = lead * s2.MBt * s2.NBt;
+  persistent_loop(a1.cnt, s1.total + s2.total, &s_next, [&](int n, auto&& drained) {
+    if (n >= splitA && n < splitA + s1.total)
+      run_tile<T, M1, false, false, true>(a1, gl, s1, n - splitA, smem, g_idx, drained);
+    else
+      run_tile<T, M2, false, false, true>(a2, gl, s2, n < splitA ? n : n - s1.total, smem, g_idx,
+                                          drained);
+  });
 }
 
 // ---------------------------------------------------------------- act recompute
@@ -1150,6 +1227,17 @@ int grid_size() {
 template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
   hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER, LIGHT>), dim3(grid_size()), dim3(NT), 0, s, a);
+  return moe_check_launch(what);
+}
+
+template <int M1, int M2>
+int launch_pair(int dt, const GmmArgs& a1, const GmmArgs& a2, hipStream_t s, const char* what) {
+  if (dt == MOE_BF16)
+    hipLaunchKernelGGL((gmm_pair_kernel<bf16_t, M1, M2>), dim3(grid_size()), dim3(NT), 0, s, a1,
+                       a2);
+  else
+    hipLaunchKernelGGL((gmm_pair_kernel<float, M1, M2>), dim3(grid_size()), dim3(NT), 0, s, a1,
+                       a2);
   return moe_check_launch(what);
 }
 
@@ -1309,12 +1397,11 @@ extern "C" int moe_grouped_gemm_fwd_gather(const void* x, const int32_t* src_tok
                   ws, ws_bytes, stream);
 }
 
-extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G,
-                                       int R, int dt, int H, int I, const void* w13,
-                                       const void* w2, const void* h13, void* dh13, void* dxp,
-                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
-                                       moe_stream_t stream) {
-  const char* fn = "moe_grouped_gemm_bwd_dx";
+namespace {
+
+int dx_checks(const char* fn, const void* dyp, const int32_t* offsets, int g0, int G, int R,
+              int dt, int H, int I, const void* w13, const void* w2, const void* h13, void* dh13,
+              void* dxp, const moe_shared_expert* sh) {
   MOE_TRY(gmm_checks(fn, offsets, g0, G, R, dt, H, I, sh));
   if (G > 0 && R > 0) {
     MOE_TRY(moe_need_ptr(dyp, fn, "dyp"));
@@ -1324,8 +1411,7 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
     MOE_TRY(moe_need_ptr(dh13, fn, "dh13"));
     MOE_TRY(moe_need_ptr(dxp, fn, "dxp"));
   }
-  const bool use_sh = sh && sh->T > 0;
-  if (use_sh) {
+  if (sh && sh->T > 0) {
     MOE_TRY(moe_need_ptr(sh->dy, fn, "shared.dy"));
     MOE_TRY(moe_need_ptr(sh->w13, fn, "shared.w13"));
     MOE_TRY(moe_need_ptr(sh->w2, fn, "shared.w2"));
@@ -1333,25 +1419,68 @@ extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, 
     MOE_TRY(moe_need_ptr(sh->dh13, fn, "shared.dh13"));
     MOE_TRY(moe_need_ptr(sh->dx, fn, "shared.dx"));
   }
-  if (!use_sh && (G == 0 || R == 0)) return MOE_OK;
-  hipStream_t s = (hipStream_t)stream;
-  GmmArgs a = base_args(offsets, g0, (R > 0) ? G : 0, R, sh);
-  MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
-  // DX1: dact = dyp . W2 (W2 stored [K=H][N=I]), SwiGLU backward into dh13
+  return MOE_OK;
+}
+
+// DX1: dact = dyp . W2 (W2 stored [K=H][N=I]), SwiGLU backward into dh13
+void dx1_args(GmmArgs& a, const void* dyp, int H, int I, const void* w2, const void* h13,
+              void* dh13, const moe_shared_expert* sh, bool use_sh) {
   a.N = I; a.K = H; a.I = I;
   a.X = dyp; a.ldx = H;
   a.W = w2; a.ldw = I; a.w_gs = (long long)H * I;
   a.C = dh13; a.ldc = 2 * I;
   a.aux = h13; a.ldaux = 2 * I;
   if (use_sh) { a.sX = sh->dy; a.sW = sh->w2; a.sC = sh->dh13; a.sAux = sh->h13; }
-  MOE_TRY(launch_dt<DX1>(dt, a, s, fn, small_groups(a.G, R)));
-  // DX2: dxp = dh13 . W13 (W13 stored [K=2I][N=H])
-  a.N = H; a.K = 2 * I;
+}
+
+// DX2: dxp = dh13 . W13 (W13 stored [K=2I][N=H])
+void dx2_args(GmmArgs& a, int H, int I, const void* w13, const void* dh13, void* dxp,
+              const moe_shared_expert* sh, bool use_sh) {
+  a.N = H; a.K = 2 * I; a.I = I;
   a.X = dh13; a.ldx = 2 * I;
   a.W = w13; a.ldw = H; a.w_gs = 2LL * I * H;
   a.C = dxp; a.ldc = H;
   a.aux = nullptr;
   if (use_sh) { a.sX = sh->dh13; a.sW = sh->w13; a.sC = sh->dx; a.sAux = nullptr; }
+}
+
+// dW2[e] [H,I] = dyp_e^T . act_e
+void dw2_args(GmmArgs& a, const void* dyp, const void* act, int H, int I, void* dw2,
+              const moe_shared_expert* sh, bool use_sh) {
+  a.M = H; a.N = I; a.I = I;
+  a.X = dyp; a.ldx = H;
+  a.W = act; a.ldw = I;
+  a.C = dw2; a.ldc = I; a.c_gs = (long long)H * I;
+  if (use_sh) { a.sX = sh->dy; a.sW = sh->act; a.sC = sh->dw2; }
+}
+
+// dW13[e] [2I,H] = dh13_e^T . xp_e
+void dw13_args(GmmArgs& a, const void* dh13, const void* xp, int H, int I, void* dw13,
+               const moe_shared_expert* sh, bool use_sh) {
+  a.M = 2 * I; a.N = H; a.I = I;
+  a.X = dh13; a.ldx = 2 * I;
+  a.W = xp; a.ldw = H;
+  a.C = dw13; a.ldc = H; a.c_gs = 2LL * I * H;
+  if (use_sh) { a.sX = sh->dh13; a.sW = sh->x; a.sC = sh->dw13; }
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_gemm_bwd_dx(const void* dyp, const int32_t* offsets, int g0, int G,
+                                       int R, int dt, int H, int I, const void* w13,
+                                       const void* w2, const void* h13, void* dh13, void* dxp,
+                                       const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                       moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_bwd_dx";
+  MOE_TRY(dx_checks(fn, dyp, offsets, g0, G, R, dt, H, I, w13, w2, h13, dh13, dxp, sh));
+  const bool use_sh = sh && sh->T > 0;
+  if (!use_sh && (G == 0 || R == 0)) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  GmmArgs a = base_args(offsets, g0, (R > 0) ? G : 0, R, sh);
+  MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
+  dx1_args(a, dyp, H, I, w2, h13, dh13, sh, use_sh);
+  MOE_TRY(launch_dt<DX1>(dt, a, s, fn, small_groups(a.G, R)));
+  dx2_args(a, H, I, w13, dh13, dxp, sh, use_sh);
   return launch_dt<DX2>(dt, a, s, fn, small_groups(a.G, R));
 }
 
@@ -1409,20 +1538,10 @@ int dw_impl(const char* fn, const void* xp, const int32_t* gather, int gather_ro
   MOE_TRY(attach_ws(a, ws, ws_bytes, fn));
   a.shared = use_sh ? 1 : 0;   // an empty shared expert still gets zero gradients
   a.shT = use_sh ? sh->T : 0;
-  // dW2[e] [H,I] = dyp_e^T . act_e
-  a.M = H; a.N = I; a.I = I;
-  a.X = dyp; a.ldx = H;
-  a.W = act; a.ldw = I;
-  a.C = dw2; a.ldc = I; a.c_gs = (long long)H * I;
-  if (use_sh) { a.sX = sh->dy; a.sW = sh->act; a.sC = sh->dw2; }
+  dw2_args(a, dyp, act, H, I, dw2, sh, use_sh);
   MOE_TRY(launch_dt<DW>(dt, a, s, fn));
-  // dW13[e] [2I,H] = dh13_e^T . xp_e
-  a.M = 2 * I; a.N = H;
-  a.X = dh13; a.ldx = 2 * I;
-  a.W = xp; a.ldw = H;
+  dw13_args(a, dh13, xp, H, I, dw13, sh, use_sh);
   a.gather = gather; a.gather_rows = gather_rows;
-  a.C = dw13; a.ldc = H; a.c_gs = 2LL * I * H;
-  if (use_sh) { a.sX = sh->dh13; a.sW = sh->x; a.sC = sh->dw13; }
   return launch_dt<DW>(dt, a, s, fn);
 }
 
@@ -1435,6 +1554,62 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
                                        moe_stream_t stream) {
   return dw_impl("moe_grouped_gemm_bwd_dw", xp, nullptr, 0, nullptr, const_cast<void*>(act), dyp,
                  dh13, offsets, g0, G, R, dt, H, I, dw13, dw2, sh, ws, ws_bytes, stream);
+}
+
+// dX and dW of one call: two persistent launches, each holding one product of
+// dX and one weight-gradient product that needs nothing from it --
+// [dact + SwiGLU bwd | dW2], then [dX | dW13] (dW13 reads the dh13 the first
+// launch wrote) -- so that neither dX product ends in a partial round of its
+// own; every output is the same bits as moe_grouped_gemm_bwd_dx followed by
+// moe_grouped_gemm_bwd_dw.  Calls whose shapes the paired launches do not
+// cover (an empty shared expert, no rows, the small-group build) take the
+// two calls' launches instead.
+extern "C" int moe_grouped_gemm_bwd(const void* xp, const void* act, const void* dyp,
+                                    const int32_t* offsets, int g0, int G, int R, int dt, int H,
+                                    int I, const void* w13, const void* w2, const void* h13,
+                                    void* dh13, void* dxp, void* dw13, void* dw2,
+                                    const moe_shared_expert* sh, void* ws, size_t ws_bytes,
+                                    moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_bwd";
+  MOE_TRY(dx_checks(fn, dyp, offsets, g0, G, R, dt, H, I, w13, w2, h13, dh13, dxp, sh));
+  if (G > 0) {
+    MOE_TRY(moe_need_ptr(dw13, fn, "dw13"));
+    MOE_TRY(moe_need_ptr(dw2, fn, "dw2"));
+    if (R > 0) {
+      MOE_TRY(moe_need_ptr(xp, fn, "xp"));
+      MOE_TRY(moe_need_ptr(act, fn, "act"));
+    }
+  }
+  const bool sh_rows = sh && sh->T > 0;
+  const bool sh_grads = sh && sh->T >= 0 && (sh->dw13 || sh->dw2);
+  if (sh_grads) {
+    MOE_TRY(moe_need_ptr(sh->dw13, fn, "shared.dw13"));
+    MOE_TRY(moe_need_ptr(sh->dw2, fn, "shared.dw2"));
+    if (sh_rows) {
+      MOE_TRY(moe_need_ptr(sh->x, fn, "shared.x"));
+      MOE_TRY(moe_need_ptr(sh->act, fn, "shared.act"));
+    }
+  }
+  // paired launches: both products on the same window (the shared expert,
+  // if any, has rows and gets its gradients), and the plain build
+  const bool paired = (G > 0 && R > 0 && !small_groups(G, R) && (!sh || (sh_rows && sh_grads))) ||
+                      (G == 0 && sh_rows && sh_grads);
+  if (!paired) {
+    MOE_TRY(moe_grouped_gemm_bwd_dx(dyp, offsets, g0, G, R, dt, H, I, w13, w2, h13, dh13, dxp, sh,
+                                    ws, ws_bytes, stream));
+    return moe_grouped_gemm_bwd_dw(xp, act, dyp, dh13, offsets, g0, G, R, dt, H, I, dw13, dw2, sh,
+                                   ws, ws_bytes, stream);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  GmmArgs a1 = base_args(offsets, g0, G, R, sh);
+  MOE_TRY(attach_ws(a1, ws, ws_bytes, fn));
+  GmmArgs a2 = a1;
+  dx1_args(a1, dyp, H, I, w2, h13, dh13, sh, sh_rows);
+  dw2_args(a2, dyp, act, H, I, dw2, sh, sh_rows);
+  MOE_TRY((launch_pair<DX1, DW>(dt, a1, a2, s, fn)));
+  dx2_args(a1, H, I, w13, dh13, dxp, sh, sh_rows);
+  dw13_args(a2, dh13, xp, H, I, dw13, sh, sh_rows);
+  return launch_pair<DX2, DW>(dt, a1, a2, s, fn);
 }
 
 extern "C" int moe_grouped_gemm_bwd_dw_recompute(const void* x, const int32_t* src_token, int T,

@@ -6,9 +6,9 @@ kernels of ``libmoe.so``.
 
 Forward:  router logits -> route -> permute -> grouped GEMM (+ shared expert)
           -> unpermute/combine.
-Backward: combine bwd -> grouped GEMM dX -> grouped GEMM dW -> route bwd ->
-          router bwd -> permute bwd (which also adds the shared expert's and
-          the router's input gradients).
+Backward: combine bwd -> grouped GEMM dX and dW (one call, paired launches)
+          -> route bwd -> router bwd -> permute bwd (which also adds the
+          shared expert's and the router's input gradients).
 
 With ``overlap`` (the default on a GPU) the work that does not depend on the
 routing runs on a second stream of the same priority: the shared expert's
@@ -248,6 +248,19 @@ class MoeLayer:
                                     G, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh, ws,
                                     self.gws_bytes, stream)
 
+    def gmm_bwd(self, stream=None, part="all"):
+        """dX and dW in one call (paired launches); the recompute variant
+        keeps its two calls (dW recomputes act and gathers x)."""
+        if self.recompute:
+            self.gmm_bwd_dx(stream, part)
+            self.gmm_bwd_dw(stream, part)
+            return
+        s = self.s
+        G, sh, ws = self._gmm_sel(part)
+        abi.moe_grouped_gemm_bwd(self.xp, self.act, self.dyp, self.offsets, s.g0, G, s.R, self.dt,
+                                 s.H, s.I, self.w13, self.w2, self.h13, self.dh13, self.dxp,
+                                 self.dw13, self.dw2, sh, ws, self.gws_bytes, stream)
+
     def route_bwd(self, stream=None):
         s = self.s
         abi.moe_route_bwd(self.logits, self.idx, self.dgate, s.T, s.E, s.k, self.dlogits, stream)
@@ -306,8 +319,7 @@ class MoeLayer:
             ev_in.record(main)
             aux.wait_event(ev_in)
             if s.shared:                                # needs dy and the forward's saves
-                self.gmm_bwd_dx(aux, part="shared")
-                self.gmm_bwd_dw(aux, part="shared")
+                self.gmm_bwd(aux, part="shared")
             self.combine_bwd(main)
             ev_c.record(main)
             aux.wait_event(ev_c)
@@ -315,15 +327,12 @@ class MoeLayer:
             if s.router:
                 self.router_bwd(aux)
             ev_aux.record(aux)
-            routed = "routed" if s.shared else "all"
-            self.gmm_bwd_dx(main, part=routed)
-            self.gmm_bwd_dw(main, part=routed)
+            self.gmm_bwd(main, part="routed" if s.shared else "all")
             main.wait_event(ev_aux)
             self.permute_bwd(main)
             return
         self.combine_bwd(stream)
-        self.gmm_bwd_dx(stream)
-        self.gmm_bwd_dw(stream)
+        self.gmm_bwd(stream)
         self.route_bwd(stream)
         if s.router:
             self.router_bwd(stream)

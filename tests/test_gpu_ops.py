@@ -244,6 +244,10 @@ GMM_CASES = [
     # per-XCD counters hand out many tiles
     ([int(c) for c in np.random.default_rng(7).integers(0, 60, 150)], 1024, 512, 0, None, 40,
      "bf16"),
+    # 40 groups of 100-600 rows with a shared expert: the paired backward
+    # launches run several rounds of both products' tiles
+    ([int(c) for c in np.random.default_rng(11).integers(100, 600, 40)], 512, 256, 0, None, 300,
+     "bf16"),
     # the largest window: 1024 experts, most of them empty or tiny
     ([int(c) for c in np.random.default_rng(9).integers(0, 4, 1024) * (
         np.random.default_rng(10).random(1024) < 0.3)], 128, 64, 0, None, 0, "bf16"),
@@ -298,9 +302,24 @@ def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt, dynamic):
                                 wsb)
     abi.moe_grouped_gemm_bwd_dw(XP, act, DYP, dh13, OFF, g0, G, R, code, H, I, dw13, dw2, sh, ws,
                                 wsb)
+    # dX and dW in one call (paired launches): the same bits
+    c_dh13, c_dxp = z(R, 2 * I), z(R, H)
+    c_dw13, c_dw2 = torch.full_like(dw13, 7.0), torch.full_like(dw2, 7.0)
+    csh = None
+    if shT:
+        cshb = dict(shb, dh13=z(shT, 2 * I), dx=z(shT, H), dw13=z(2 * I, H), dw2=z(H, I))
+        csh = abi.shared_expert(T=shT, **cshb)
+    abi.moe_grouped_gemm_bwd(XP, act, DYP, OFF, g0, G, R, code, H, I, W13, W2, h13, c_dh13, c_dxp,
+                             c_dw13, c_dw2, csh, ws, wsb)
     torch.cuda.synchronize()
     if dynamic:   # every call leaves the scheduler counters at zero
         assert int(ws.to(torch.int32).sum()) == 0
+    for name, a, b in (("dh13", dh13, c_dh13), ("dxp", dxp, c_dxp), ("dw13", dw13[:G], c_dw13[:G]),
+                       ("dw2", dw2[:G], c_dw2[:G])):
+        assert torch.equal(a, b), name
+    if shT:
+        for n in ("dh13", "dx", "dw13", "dw2"):
+            assert torch.equal(shb[n], cshb[n]), "shared " + n
     if E:
         rdh13, rdxp, rdw13, rdw2 = oracle.grouped_backward(xp, dyp, offsets, w13, w2, g0, G)
         assert rel_err(host(dh13), rdh13) <= tol
