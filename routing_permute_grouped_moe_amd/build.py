@@ -47,9 +47,10 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
     # The grouped GEMM counts its own buffer loads (hand-written waits on the
-    # vector-memory counter around the LDS copies); a kernel that spills
-    # registers to scratch adds memory operations of its own, and such a build
-    # has given wrong results.  No kernel of the library may spill.
+    # vector-memory counter around the LDS copies) and sizes its register use
+    # to keep one or two waves per SIMD; a spill would add memory operations
+    # those waits do not expect and scratch traffic in the main loop.  No
+    # kernel of the library may spill.
     bad = _scratch_kernels(r.stderr)
     if bad:
         raise RuntimeError(f"{src}: kernels spill registers to scratch: {bad}")

@@ -41,9 +41,22 @@
 
 namespace {
 
-constexpr int BM = 256, BN = 256, NT = 256;
-constexpr int WTM = 128, WTN = 128;  // wave tile
-constexpr int FM = 4, FN = 4;        // 32x32 fragments per wave tile
+constexpr int BM = 256, BN = 256;
+constexpr int WTM = 128;             // wave tile rows (two wave rows per tile)
+constexpr int FM = 4;                // 32-row fragments per wave tile
+
+// W wavefronts per workgroup: 2 wave rows x W/2 wave columns.  W = 4 gives
+// each wave a 128 x 128 tile (4 x 4 fragments, accumulators in the AGPRs,
+// one wave per SIMD); W = 8 gives 128 x 64 (4 x 2 fragments, two waves per
+// SIMD, so one wave's MFMAs run while the other waits on LDS or a barrier).
+template <int W>
+struct Waves {
+  static constexpr int NT = 64 * W;    // threads per workgroup
+  static constexpr int WN = W / 2;     // wave columns
+  static constexpr int FN = 16 / W;    // 32-column fragments per wave tile
+  static constexpr int WTN = 32 * FN;  // wave tile columns
+  static constexpr int HW = WTN / 2;   // a wave's columns in one epilogue slice
+};
 constexpr int RING_BYTES = 131072;   // LDS ring of operand stages (also the epilogue slice)
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
 constexpr int EP_PITCH = 128;        // floats per LDS row of an epilogue slice (128 KB in all)
@@ -86,17 +99,18 @@ struct GmmArgs {
 };
 
 // Per element type: K step BK (KS MFMA k-steps), ring of STAGES stages of two
-// OPB-byte operand tiles, ROWB bytes per K-major tile row, DPO 1 KB copies
-// per wave per operand per K step.
+// OPB-byte operand tiles, ROWB bytes per K-major tile row.
 template <typename T> struct Cfg;
 template <> struct Cfg<bf16_t> {
   static constexpr int ES = 2, VEC = 8, BK = 32, KS = 2;   // 2 MFMA k-steps of 16
-  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64, DPO = OPB / 1024 / (NT / 64);
+  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64;
 };
 template <> struct Cfg<float> {
   static constexpr int ES = 4, VEC = 4, BK = 16, KS = 8;   // 8 MFMA k-steps of 2
-  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64, DPO = OPB / 1024 / (NT / 64);
+  static constexpr int STAGES = 4, OPB = 16384, ROWB = 64;
 };
+// 1 KB copies per wave per operand per K step
+template <typename T, int W> constexpr int DPO_OF = Cfg<T>::OPB / 1024 / W;
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -136,12 +150,18 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // One 1 KB HBM -> LDS copy: lane l's 16 bytes at voff + soff land at
 // lds + 16 l.  Issued as inline assembly so that the compiler does not guard
 // every later LDS read with a wait on all outstanding copies; the kernel
-// waits for exactly the copies it needs (wait_vm) before a barrier.
+// waits for exactly the copies it needs (wait_vm) before a barrier.  The LDS
+// address goes through M0, and an LDS-DMA load needs one wait state after
+// the write of M0 (the compiler's hazard checks do not look inside inline
+// assembly): M0 is written here, followed by s_nop 0.  Without the nop, a
+// copy issued right after its M0 write could land at the previous copy's
+// LDS address (seen as wrong, non-deterministic weight gradients whenever
+// the scheduler put the two instructions back to back).
 __device__ __forceinline__ void dma16(const i32x4& rs, uint32_t lds, uint32_t voff, int soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(uniform(soff)), "{m0}"(uniform((int)lds))
-               : "memory");
+               : "v"(voff), "s"(rs), "s"(uniform(soff)), "s"(uniform((int)lds))
+               : "memory", "m0");
 }
 
 // Wait until at most n of this wave's buffer loads are outstanding.
@@ -182,10 +202,11 @@ __device__ __forceinline__ View make_view(const void* base, long long bytes, int
 //
 // K-major: a copy covers 1024 / ROWB whole rows; lane l fills row
 // q * RPC + l / LPR, slot l % LPR, from the chunk that belongs in that slot.
-template <typename T, bool SWIGLU>
+template <typename T, bool SWIGLU, int W>
 __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
-                                               uint32_t (&off)[Cfg<T>::DPO]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
+                                               uint32_t (&off)[DPO_OF<T, W>]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
+  constexpr int WTN = Waves<W>::WTN, HW = Waves<W>::HW;
   constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;   // lanes per row, rows per copy
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -196,11 +217,12 @@ __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
     int src;
     bool ok;
     if (SWIGLU) {
-      // per wave column block of 128 rows: rows [128w, 128w+64) are gate rows
-      // i0+64w+c, rows [128w+64, 128w+128) the up rows I+i0+64w+c (i0 = mn0)
-      const int w = row >> 7, r = row & 127;
-      const int c = w * 64 + (r & 63);
-      src = ((r >> 6) ? I : 0) + mn0 + c;
+      // per wave column block of WTN rows: rows [WTN w, WTN w + HW) are gate
+      // rows i0 + HW w + c, the next HW rows the up rows I + i0 + HW w + c
+      // (i0 = mn0)
+      const int w = row / WTN, r = row % WTN;
+      const int c = w * HW + (r % HW);
+      src = ((r / HW) ? I : 0) + mn0 + c;
       ok = mn0 + c < I;
     } else {
       src = mn0 + row;
@@ -212,10 +234,10 @@ __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
 
 // MN-major: bf16 copy q covers K rows 2q, 2q+1 (lane l: row 2q + l/32, slot
 // l%32); fp32 copy q covers K row q (lane l: slot l).
-template <typename T>
+template <typename T, int W>
 __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
-                                                uint32_t (&off)[Cfg<T>::DPO]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
+                                                uint32_t (&off)[DPO_OF<T, W>]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < DPO; ++j) {
@@ -235,11 +257,11 @@ __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
 
 // K-major, rows gathered: tile row `row` (< rows) is row gather[rows0 + row]
 // of the view; the indices are read once per tile.
-template <typename T>
+template <typename T, int W>
 __device__ __forceinline__ void kmajor_offsets_gather(const View& v, const int32_t* gather,
                                                       int rows0, int rows,
-                                                      uint32_t (&off)[Cfg<T>::DPO]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = Cfg<T>::DPO;
+                                                      uint32_t (&off)[DPO_OF<T, W>]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
   constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t gi = make_rsrc(gather + rows0, (uint32_t)rows * 4u);
@@ -261,10 +283,10 @@ __device__ __forceinline__ void kmajor_offsets_gather(const View& v, const int32
 // One 256-byte HBM -> LDS copy of 4-byte words: lane l's word at voff + soff
 // lands at lds + 4 l (the row indices of a gathered operand).
 __device__ __forceinline__ void dma4(const i32x4& rs, uint32_t lds, uint32_t voff, int soff) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(uniform(soff)), "{m0}"(uniform((int)lds))
-               : "memory");
+               : "v"(voff), "s"(rs), "s"(uniform(soff)), "s"(uniform((int)lds))
+               : "memory", "m0");
 }
 
 template <int DPO>
@@ -315,8 +337,9 @@ __device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
 // n = 32 j + 8 (r/4) + 4 (lane/32) + r%4: every lane owns runs of four
 // consecutive output columns, which the epilogue writes to LDS as one
 // 16-byte store.
-template <typename T, bool A_MN, bool B_MN>
+template <typename T, bool A_MN, bool B_MN, int W>
 struct Frags {
+  static constexpr int FN = Waves<W>::FN, WTN = Waves<W>::WTN;
   decltype(read_frag<T, A_MN>(nullptr, 0, 0)) a[FM];
   decltype(read_frag<T, B_MN>(nullptr, 0, 0)) b[FN];
   __device__ __forceinline__ void load(const char* la, const char* lb, int wm, int wn, int ks) {
@@ -374,7 +397,7 @@ struct Space {
 // Row ranges of the window's groups (and of the shared expert as group G).
 __device__ __forceinline__ void load_groups(const GmmArgs& a, GroupLds& gl) {
   const int ng = a.G + a.shared;
-  for (int g = threadIdx.x; g < ng; g += NT) {
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) {
     int lo, hi;
     if (g < a.G && !a.dense) {
       lo = a.offsets[a.g0 + g];
@@ -417,7 +440,7 @@ __device__ __forceinline__ void tile_prefix(int ng, GroupLds& gl) {
 
 // Group order by descending row count (stable) into gl.ord.
 __device__ __forceinline__ void group_order(int ng, GroupLds& gl) {
-  for (int g = threadIdx.x; g < ng; g += NT) {
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) {
     const int c = gl.hi[g] - gl.lo[g];
     int rank = 0;
     for (int h = 0; h < ng; ++h) {
@@ -475,9 +498,10 @@ __device__ __forceinline__ Space tile_space(const GmmArgs& a, const GroupLds& gl
 // 128 KB operand ring (also the epilogue's staging), g_idx the gathered-row
 // index ring.  drained() runs once per tile, by every thread, at the point
 // where every copy of the tile and the scheduler's draw have landed.
-template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, typename Drained>
+template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, typename Drained>
 __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
                                          int tile_id, char* smem, int* g_idx, Drained&& drained) {
+  constexpr int NT = Waves<W>::NT, WN = Waves<W>::WN, FN = Waves<W>::FN, HW = Waves<W>::HW;
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   // DW with gathered Q rows: the rows change every K step, so each wave also
   // copies its K rows' indices into an LDS ring, two steps before the copies
@@ -487,16 +511,18 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   static_assert(!GATHER || MODE == FWD1 || MODE == DW, "rows are gathered in FWD1 and DW");
   static_assert(!LIGHT || (MODE != DW && sizeof(T) == 2), "light builds: bf16 row-tiled modes");
   static_assert(!GLOOP || sizeof(T) == 2, "gathered DW is built for bf16");
+  static_assert(W == 4 || (W == 8 && sizeof(T) == 2 && !GLOOP),
+                "8 waves: bf16, without the gathered weight-gradient index ring");
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
   constexpr int STAGES = Cfg<T>::STAGES, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
-  constexpr int DMA_PER_OP = Cfg<T>::DPO;
+  constexpr int DMA_PER_OP = DPO_OF<T, W>;
   constexpr int DMA_PER_STEP = 2 * DMA_PER_OP;   // buffer loads per wave per K step
   static_assert(STAGES * STAGE_BYTES == RING_BYTES, "stage ring size");
   static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 wave grid
+  const int wm = wave / WN, wn = wave % WN;   // 2 x WN wave grid
   const int ng = a.G + a.shared;
   // ---- locate the tile
   int g, m0, n0, rows0 = 0, rows = 0, kdim;
@@ -576,18 +602,18 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
 
   const int KT = (kdim + BK - 1) / BK;   // K steps with data
   uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
-  if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
+  if constexpr (A_MN) mnmajor_offsets<T, W>(va, m0, offa);
   else if (GATHER && MODE == FWD1 && gat)
-    kmajor_offsets_gather<T>(va, a.gather, rows0, rows, offa);
-  else kmajor_offsets<T, false>(va, m0, 0, offa);
+    kmajor_offsets_gather<T, W>(va, a.gather, rows0, rows, offa);
+  else kmajor_offsets<T, false, W>(va, m0, 0, offa);
   if constexpr (GLOOP) {
     // gathered Q: only the column part is fixed; the row part comes with
     // each K step's indices (view with ld 0 gives column offsets)
     View vc = vb;
     if (gat) vc.ld = 0;
-    mnmajor_offsets<T>(vc, n0, offb);
-  } else if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
-  else kmajor_offsets<T, MODE == FWD1>(vb, n0, a.I, offb);
+    mnmajor_offsets<T, W>(vc, n0, offb);
+  } else if constexpr (B_MN) mnmajor_offsets<T, W>(vb, n0, offb);
+  else kmajor_offsets<T, MODE == FWD1, W>(vb, n0, a.I, offb);
   const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
   const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
   const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
@@ -703,7 +729,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
         constexpr int FA = decltype(fa_c)::value;
         // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
         auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
-        Frags<T, A_MN, B_MN> f0, f1;
+        Frags<T, A_MN, B_MN, W> f0, f1;
 #pragma unroll
         for (int q = 0; q < FM + FN; ++q)
           if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
@@ -753,7 +779,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           default: kloop(std::integral_constant<int, FM>{}); break;
         }
       } else {
-        Frags<T, A_MN, B_MN> f0, f1;
+        Frags<T, A_MN, B_MN, W> f0, f1;
         f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
         for (int kt = 0; kt < KT; ++kt) {
           const char* cs = stage(kt);
@@ -798,7 +824,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
         }
       }
     } else {
-      Frags<T, A_MN, B_MN> cur, nxt;
+      Frags<T, A_MN, B_MN, W> cur, nxt;
       cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -835,20 +861,21 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   __syncthreads();   // every wave is done with the ring
   float* ep = (float*)smem;
   auto put = [&](auto fn0c, auto&& value) {
-    // fragments fn0, fn0+1 of each wave -> LDS columns wn*64 + j*32 + (0..31)
-    // (fn0 is a compile-time constant so the accumulators stay in registers);
-    // 16-byte granule g of row m sits at g ^ (m % 32), so the 32 rows of a
-    // store and the 16 chunks of a row read all hit distinct banks
+    // fragments fn0 .. fn0 + FN/2 - 1 of each wave -> LDS columns
+    // wn*HW + j*32 + (0..31) (fn0 is a compile-time constant so the
+    // accumulators stay in registers); 16-byte granule g of row m sits at
+    // g ^ (m % 32), so the 32 rows of a store and the 16 chunks of a row read
+    // all hit distinct banks
     constexpr int slice_fn0 = decltype(fn0c)::value;
     const int m = elane & 31;
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < FN / 2; ++j)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int row = wm * WTM + f * 32 + m;
-          const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
+          const int g = (wn * HW + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
           f32x4 v;
           v.x = value(f, slice_fn0 + j, rq * 4 + 0);
           v.y = value(f, slice_fn0 + j, rq * 4 + 1);
@@ -859,9 +886,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     __syncthreads();
   };
   auto take = [&](auto&& consume) {
-    // 256 rows x 16 chunks of 8 columns, 16 per thread
+    // 256 rows x 16 chunks of 8 columns, 4096 / NT per thread
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < 4096 / NT; ++it) {
       const int idx = it * NT + etid;
       const int row = idx >> 4, cc = (idx & 15) * 8;
       const int sw = row & 31;
@@ -879,7 +906,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   // slice sl of the finished tile -> consume(row, c, v[8])
   auto emit = [&](auto slc, auto&& consume) {
     constexpr int sl = decltype(slc)::value;
-    put(std::integral_constant<int, 2 * sl>{}, acc_of);
+    put(std::integral_constant<int, sl * (FN / 2)>{}, acc_of);
     take(consume);
   };
 
@@ -905,8 +932,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     }
   };
   if constexpr (MODE == FWD1) {
-    // fragments 0,1 of a wave hold gate columns i0 + wn*64 + j*32 + elane%32,
-    // fragments 2,3 the matching up columns; LDS column c is i = i0 + c
+    // fragments 0 .. FN/2-1 of a wave hold gate columns i0 + wn*HW + j*32 +
+    // elane%32, fragments FN/2 .. FN-1 the matching up columns; LDS column c
+    // is i = i0 + c
     void* hb = sh ? a.sC : a.C;
     void* ab = sh ? a.sC2 : a.C2;
     const __amdgpu_buffer_rsrc_t hr = make_rsrc((char*)hb + (long long)rows0 * a.ldc * ES,
@@ -932,15 +960,16 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
 #pragma unroll
       for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN / 2; ++j)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             const int row = wm * WTM + f * 32 + m;
-            const int g = (wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
+            const int g = (wn * HW + j * 32 + rq * 8 + (elane >> 5) * 4) >> 2;
             f32x4* pp = (f32x4*)(ep + row * EP_PITCH + ((g ^ m) << 2));
             f32x4 v = *pp;
-            const f32x4 u = {acc[f][2 + j][rq * 4 + 0], acc[f][2 + j][rq * 4 + 1],
-                             acc[f][2 + j][rq * 4 + 2], acc[f][2 + j][rq * 4 + 3]};
+            constexpr int U = FN / 2;
+            const f32x4 u = {acc[f][U + j][rq * 4 + 0], acc[f][U + j][rq * 4 + 1],
+                             acc[f][U + j][rq * 4 + 2], acc[f][U + j][rq * 4 + 3]};
             v.x = swiglu_act<T>(v.x, u.x);
             v.y = swiglu_act<T>(v.y, u.y);
             v.z = swiglu_act<T>(v.z, u.z);
@@ -950,10 +979,10 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       __syncthreads();
     }
     take(store_act);
-    put(std::integral_constant<int, 2>{}, acc_of);
+    put(std::integral_constant<int, FN / 2>{}, acc_of);
     take(store_up);
   } else {
-    // LDS column c of slice h is tile column (c/64)*128 + 64h + c%64
+    // LDS column c of slice h is tile column (c/HW)*WTN + HW h + c%HW
     auto slice = [&](auto hc) {
       constexpr int h = decltype(hc)::value;
       if constexpr (MODE == DX1) {
@@ -977,7 +1006,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           store8(dr, ok, (uint32_t)(row * a.ldc + a.I + i), du);
         };
         if (sizeof(T) == 2) {
-          // bf16: the slice's gate/up chunks (16 per thread) are
+          // bf16: the slice's gate/up chunks (4096 / NT per thread) are
           // requested before the accumulators are staged, so their latency
           // hides behind the LDS round trip instead of serializing with the
           // stores (a load may not pass an earlier store to a buffer that
@@ -985,12 +1014,13 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           // half is requested after the first half's stores), which keeps a
           // kernel that also holds another product's code within the
           // register file
-          constexpr int PF = LEAN ? 8 : 16;
+          constexpr int CH = 4096 / NT;          // chunks per thread
+          constexpr int PF = LEAN ? CH / 2 : CH;
           u32x4 graw[PF], uraw[PF];
           auto fetch = [&](int it) {
             const int idx = it * NT + etid;
             const int row = idx >> 4, cc = (idx & 15) * 8;
-            const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+            const int i = n0 + (cc / HW) * (2 * HW) + HW * h + (cc % HW);
             const bool ok = row < rows && i < a.I;
             graw[it % PF] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + i) * 2u : OOB);
             uraw[it % PF] = buf_load16(hr, ok ? (uint32_t)(row * a.ldaux + a.I + i) * 2u : OOB);
@@ -1002,7 +1032,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
             const f32x4 lo = *(const f32x4*)(ep + row * EP_PITCH + (((cc >> 2) ^ sw) << 2));
             const f32x4 hi = *(const f32x4*)(ep + row * EP_PITCH + ((((cc >> 2) + 1) ^ sw) << 2));
             const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            const int i = n0 + (cc >> 6) * 128 + 64 * h + (cc & 63);
+            const int i = n0 + (cc / HW) * (2 * HW) + HW * h + (cc % HW);
             float gv[8], uv[8];
             unpack16(graw[it % PF], gv, T());
             unpack16(uraw[it % PF], uv, T());
@@ -1011,25 +1041,25 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           // first half requested before the staging, second half after it
           // (ahead of the first half's stores; LEAN: after them)
 #pragma unroll
-          for (int it = 0; it < 8; ++it) fetch(it);
-          put(std::integral_constant<int, 2 * h>{}, acc_of);
+          for (int it = 0; it < CH / 2; ++it) fetch(it);
+          put(std::integral_constant<int, h * (FN / 2)>{}, acc_of);
           if constexpr (LEAN) {
 #pragma unroll
-            for (int it = 0; it < 8; ++it) finish(it);
+            for (int it = 0; it < CH / 2; ++it) finish(it);
 #pragma unroll
-            for (int it = 8; it < 16; ++it) fetch(it);
+            for (int it = CH / 2; it < CH; ++it) fetch(it);
 #pragma unroll
-            for (int it = 8; it < 16; ++it) finish(it);
+            for (int it = CH / 2; it < CH; ++it) finish(it);
           } else {
 #pragma unroll
-            for (int it = 8; it < 16; ++it) fetch(it);
+            for (int it = CH / 2; it < CH; ++it) fetch(it);
 #pragma unroll
-            for (int it = 0; it < 16; ++it) finish(it);
+            for (int it = 0; it < CH; ++it) finish(it);
           }
           __syncthreads();
         } else {
           emit(hc, [&](int row, int c, const float* d) {
-            const int i = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+            const int i = n0 + (c / HW) * (2 * HW) + HW * h + (c % HW);
             const bool ok = row < rows && i < a.I;
             float gv[8], uv[8];
             load8(hr, ok, (uint32_t)(row * a.ldaux + i), gv);
@@ -1057,7 +1087,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
         // (the output type is chosen outside the loop, which then
         // unrolls into batches of LDS reads and stores)
         auto place = [&](int row, int c, bool& ok) {
-          const int n = n0 + (c >> 6) * 128 + 64 * h + (c & 63);
+          const int n = n0 + (c / HW) * (2 * HW) + HW * h + (c % HW);
           const int m = m0 + row;
           ok = m < lim_m && n < a.N;
           return (uint32_t)(m * a.ldc + n);
@@ -1135,9 +1165,10 @@ __device__ __forceinline__ void persistent_loop(int* ctr, int total, int* s_next
   }
 }
 
-template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
-__global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
+template <typename T, int MODE, bool GATHER = false, bool LIGHT = false, int W = 4>
+__global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
   constexpr bool GLOOP = GATHER && MODE == DW;
+  constexpr int NT = Waves<W>::NT;
   __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
   __shared__ GroupLds gl;
   __shared__ int s_next;
@@ -1149,7 +1180,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
   else group_order(ng, gl);
   const Space sp = tile_space<MODE, LIGHT>(a, gl, &s_next);
   persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained) {
-    run_tile<T, MODE, GATHER, LIGHT, false>(a, gl, sp, n, smem, g_idx, drained);
+    run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained);
   });
 }
 
@@ -1159,8 +1190,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_kernel(GmmArgs a) {
 // whose K (rows) is at least the row-tiled product's K run first, then the
 // row-tiled product, then the remaining (short) gradient tiles, which fill
 // the last round.
-template <typename T, int M1, int M2>
-__global__ __launch_bounds__(NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2) {
+template <typename T, int M1, int M2, int W>
+__global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2) {
   static_assert(M1 != DW && M2 == DW, "a row-tiled product and a weight-gradient product");
   __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
   __shared__ GroupLds gl;
@@ -1178,10 +1209,10 @@ __global__ __launch_bounds__(NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2)
   const int splitA = lead * s2.MBt * s2.NBt;
   persistent_loop(a1.cnt, s1.total + s2.total, &s_next, [&](int n, auto&& drained) {
     if (n >= splitA && n < splitA + s1.total)
-      run_tile<T, M1, false, false, true>(a1, gl, s1, n - splitA, smem, g_idx, drained);
+      run_tile<T, M1, false, false, true, W>(a1, gl, s1, n - splitA, smem, g_idx, drained);
     else
-      run_tile<T, M2, false, false, true>(a2, gl, s2, n < splitA ? n : n - s1.total, smem, g_idx,
-                                          drained);
+      run_tile<T, M2, false, false, true, W>(a2, gl, s2, n < splitA ? n : n - s1.total, smem,
+                                             g_idx, drained);
   });
 }
 
@@ -1224,20 +1255,31 @@ int grid_size() {
   return n >= 8 ? (n / 8) * 8 : n;
 }
 
+// Workgroup shape: 4 waves.  The 8-wave shape (bf16 only) passes every
+// parity test but measured slower on the Pangu share (gate/up product 669
+// against 648 us, layer step 4.35 against 4.15 ms) although a bare main-loop
+// microbenchmark ran it 5-14% faster (a higher clock at the same cycles per
+// K step); its epilogues take longer with half the columns per wave.
+template <typename T, int MODE, bool GATHER>
+constexpr int WAVES = 4;
+
 template <typename T, int MODE, bool GATHER = false, bool LIGHT = false>
 int launch(const GmmArgs& a, hipStream_t s, const char* what) {
-  hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER, LIGHT>), dim3(grid_size()), dim3(NT), 0, s, a);
+  constexpr int W = WAVES<T, MODE, GATHER>;
+  hipLaunchKernelGGL((gmm_kernel<T, MODE, GATHER, LIGHT, W>), dim3(grid_size()),
+                     dim3(Waves<W>::NT), 0, s, a);
   return moe_check_launch(what);
 }
 
 template <int M1, int M2>
 int launch_pair(int dt, const GmmArgs& a1, const GmmArgs& a2, hipStream_t s, const char* what) {
   if (dt == MOE_BF16)
-    hipLaunchKernelGGL((gmm_pair_kernel<bf16_t, M1, M2>), dim3(grid_size()), dim3(NT), 0, s, a1,
+    hipLaunchKernelGGL((gmm_pair_kernel<bf16_t, M1, M2, WAVES<bf16_t, M1, false>>),
+                       dim3(grid_size()), dim3(Waves<WAVES<bf16_t, M1, false>>::NT), 0, s, a1,
                        a2);
   else
-    hipLaunchKernelGGL((gmm_pair_kernel<float, M1, M2>), dim3(grid_size()), dim3(NT), 0, s, a1,
-                       a2);
+    hipLaunchKernelGGL((gmm_pair_kernel<float, M1, M2, 4>), dim3(grid_size()),
+                       dim3(Waves<4>::NT), 0, s, a1, a2);
   return moe_check_launch(what);
 }
 
