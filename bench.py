@@ -44,9 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the timing of the recompute variant")
-    p.add_argument("--sequential", action="store_true",
-                   help="time steps with every call on one stream (the per-call breakdown is "
-                        "always measured that way)")
+    p.add_argument("--overlap", action="store_true",
+                   help="time steps with the route and router backward on a second stream "
+                        "(default: every call on one stream, as the per-call breakdown)")
     p.add_argument("--cpu-tokens", type=int, default=8192,
                    help="tokens in the oracle's timed sample")
     p.add_argument("--no-dense-ref", action="store_true",
@@ -305,7 +305,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    L.overlap = L.overlap and not args.sequential
+    L.overlap = args.overlap
     for _ in range(args.warmup):
         L.step()
     torch.cuda.synchronize()
@@ -313,8 +313,8 @@ def main():
     rows_local = int(rows[cfg.g0 + cfg.groups] - rows[cfg.g0])
     active_local = int((L.counts.cpu().numpy()[cfg.g0:cfg.g0 + cfg.groups] > 0).sum())
 
-    # timed region: K whole steps (the shared expert and the router backward on
-    # a second stream unless --sequential), bracketed by device synchronisation
+    # timed region: K whole steps (the route and router backward on a second
+    # stream with --overlap), bracketed by device synchronisation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):

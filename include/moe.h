@@ -239,15 +239,19 @@ int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row
  * T rows in the same launch (a dense group with its own weights).
  * Arithmetic: dt products, fp32 accumulation; outputs stored as dt.
  *
- * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes, 256-byte
- * aligned, holding the tile scheduler's counters.  It must be zero-filled
- * before its first use; every call returns it to zero when it completes.
- * With it, the workgroups of each XCD take their tiles from a shared counter
- * (a workgroup that starts late, e.g. while another kernel still holds its
- * CU, just takes fewer tiles); with ws == NULL they take a fixed share.
- * Results are identical either way (each tile is computed whole, in the same
- * order, by one workgroup).  Calls that run concurrently (on different
- * streams) need separate workspaces.
+ * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes (64 KiB plus
+ * 256), 256-byte aligned, holding the tile scheduler's counters and the
+ * forward's per-row-tile completion counters.  It must be zero-filled before
+ * its first use; every call returns it to zero when it completes.  With it,
+ * the workgroups of each XCD take their tiles from a shared counter (a
+ * workgroup that starts late, e.g. while another kernel still holds its CU,
+ * just takes fewer tiles) and the forward runs as one launch (below); with
+ * ws == NULL they take a fixed share.  Results are identical either way
+ * (each tile is computed whole, in the same order, by one workgroup).  Calls
+ * that run concurrently (on different streams) need separate workspaces.
+ * The int at byte offset 44 is a sticky error word: a forward wait that
+ * ran past one second (only possible when concurrent calls share a
+ * workspace) gives up and sets it to 1; it is never cleared by the library.
  */
 size_t moe_gmm_workspace_bytes(void);
 typedef struct moe_shared_expert {
@@ -270,7 +274,12 @@ typedef struct moe_shared_expert {
  *           yp  = act . w2[e]^T        ([R,H])
  * The activation is computed in fp32 from the gate and up values as h13
  * stores them (rounded to dt), so the backward, which reads h13, and
- * moe_grouped_gemm_bwd_dw_recompute see the same g and u. */
+ * moe_grouped_gemm_bwd_dw_recompute see the same g and u.
+ * With a workspace, both products run in one persistent launch: a row
+ * tile's yp tiles start once every h13/act tile of that row tile is stored
+ * (per-row-tile counters), so the second product fills the rounds the first
+ * leaves partly idle.  Groups averaging half a tile or less, and windows of
+ * more than 16384 row tiles, run as two launches. */
 int moe_grouped_gemm_fwd(const void* xp, const int32_t* offsets, int g0, int G, int R,
                          int dt, int H, int I, const void* w13, const void* w2,
                          void* h13, void* act, void* yp, const moe_shared_expert* shared,

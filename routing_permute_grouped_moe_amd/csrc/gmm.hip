@@ -498,7 +498,8 @@ __device__ __forceinline__ Space tile_space(const GmmArgs& a, const GroupLds& gl
 // 128 KB operand ring (also the epilogue's staging), g_idx the gathered-row
 // index ring.  drained() runs once per tile, by every thread, at the point
 // where every copy of the tile and the scheduler's draw have landed.
-template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, typename Drained>
+template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, bool ACT_DEV = false,
+          typename Drained>
 __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
                                          int tile_id, char* smem, int* g_idx, Drained&& drained) {
   constexpr int NT = Waves<W>::NT, WN = Waves<W>::WN, FN = Waves<W>::FN, HW = Waves<W>::HW;
@@ -922,6 +923,16 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       buf_store16_nt(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
     }
   };
+  // act rows another XCD reads within the same launch: stored at device
+  // scope, so they are visible everywhere once the stores have completed
+  auto store8_dev = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, const float* v) {
+    if constexpr (sizeof(T) == 2) {
+      buf_store16_dev(rs, ok ? elem * 2u : DROP, pack16(v, T()));
+    } else {
+      buf_store16_dev(rs, ok ? elem * 4u : DROP, pack16(v, T()));
+      buf_store16_dev(rs, ok ? elem * 4u + 16u : DROP, pack16(v + 4, T()));
+    }
+  };
   // 8 values at element elem of an operand (zeros unless ok)
   auto load8 = [&](const __amdgpu_buffer_rsrc_t& rs, bool ok, uint32_t elem, float* v) {
     if constexpr (sizeof(T) == 2) {
@@ -948,7 +959,10 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       store8(hr, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc + a.I + n0 + c), v);
     };
     auto store_act = [&](int row, int c, const float* v) {
-      store8(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
+      if constexpr (ACT_DEV)
+        store8_dev(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
+      else
+        store8(ar, row < rows && n0 + c < a.I, (uint32_t)(row * a.ldc2 + n0 + c), v);
     };
     // gate slice out; then act = silu(g) * u replaces it in LDS (each
     // elane rewrites the very words it put, so no barrier in between and
@@ -1216,6 +1230,175 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, G
   });
 }
 
+// ---------------------------------------------------------------- forward chain
+// Both forward products in one persistent launch: every gate/up tile first,
+// then the act . W2^T tiles, each of which starts once every gate/up tile
+// of its row tile has stored its act rows.  The second product's first
+// tiles fill the round the first product leaves partly idle, and the
+// launch ends in one tail of short second-product tiles instead of two.
+// (Interleaving the products band by band was measured slower: a
+// second-product tile claimed one band after its row tile's first-product
+// tiles waited ~50 us for them on the Pangu share, as first-product tiles
+// are ~4x longer.)  The workgroups of each XCD take positions of this order
+// from their XCD's counter, in the same chunks as the single-product
+// launches (so an XCD's workgroups share operand panels in its L2).
+//
+// Progress does not depend on which workgroups are resident: a workgroup
+// owns a first-product tile only once it has exchanged the tile's start
+// word from 0 to 1, right before running it, and a second-product tile
+// whose dependencies are not finished runs every first-product tile of its
+// M-tile that nobody has started yet itself.  So it only ever waits for
+// tiles that a running workgroup is computing, and those have no
+// dependencies -- also beside another chained launch on another stream.
+//
+// Workspace ints after the single-product scheduler's nine: the finished-
+// workgroup counter, a sticky error word, 8 per-XCD position counters, and
+// from CH_DEP on one completion counter per M-tile, then from CH_ST on one
+// start word per first-product tile (all zero on entry and on exit).
+constexpr int CH_DONE = 10, CH_ERR = 11, CH_XCD = 16, CH_DEP = 64;
+constexpr int CH_MAX_MT = 16384;                 // M-tiles a chained launch can track
+constexpr int CH_ST = CH_DEP + CH_MAX_MT;
+constexpr int CH_MAX_T1 = 65536;                 // first-product tiles it can track
+constexpr unsigned long long CH_WAIT_TICKS = 100000000ull;   // 1 s of the 100 MHz clock
+
+// M-tile of tile t of a row-tiled product with NB N-tiles, and tile of
+// (M-tile mi, N-tile nbi) -- the band order of run_tile.
+__device__ __forceinline__ int mtile_of(int t, int NB, int MT) {
+  const int band = GM_BAND * NB;
+  const int first = (t / band) * GM_BAND;
+  return first + (t % band) % min(GM_BAND, MT - first);
+}
+__device__ __forceinline__ int tile_at(int mi, int nbi, int NB, int MT) {
+  const int first = mi / GM_BAND * GM_BAND;
+  return first * NB + (mi - first) + nbi * min(GM_BAND, MT - first);
+}
+
+template <typename T, bool GATHER, int W>
+__global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_chain_kernel(GmmArgs a1, GmmArgs a2) {
+  constexpr int NT = Waves<W>::NT;
+  __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
+  __shared__ GroupLds gl;
+  __shared__ int s_next, s_cmd;
+  __shared__ int g_idx[4];
+  const int tid = threadIdx.x;
+  const int ng = a1.G + a1.shared;
+  load_groups(a1, gl);
+  tile_prefix(ng, gl);
+  const Space s1 = tile_space<FWD1, false>(a1, gl, &s_next);
+  const Space s2 = tile_space<FWD2, false>(a2, gl, &s_next);
+  const int MT = gl.pre[ng];
+  const int total1 = s1.total, total = s1.total + s2.total;
+  int* const ws = a1.cnt;
+  int* const dep = ws + CH_DEP;
+  int* const st = ws + CH_ST;
+  const int nwg = gridDim.x;
+  const int nx = (nwg % 8 == 0) ? 8 : 1;
+  const int xcd = blockIdx.x % nx, wpx = nwg / nx;
+  int* const ctr = ws + CH_XCD + xcd;
+  // n-th position of this XCD's sequence
+  auto pos_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
+  auto draw = [&]() {
+    return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto take = [&](int t) {   // thread 0: start first-product tile t unless started
+    return __hip_atomic_exchange(st + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+  };
+  auto first_tile = [&](int t, auto&& drained) {
+    run_tile<T, FWD1, GATHER, false, false, W, true>(a1, gl, s1, t, smem, g_idx, drained);
+    // publish: the act rows were stored at device scope (write-through), so
+    // once every wave's stores have completed the count can go out -- the
+    // compiler's agent-scope release for such stores is this same wait.  (A
+    // release fence would also write back the whole L2 of this XCD, which
+    // measured 8% of the launch for the small config's short tiles; h13 is
+    // read by later launches only.)
+    wait_vm<0>();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(dep + mtile_of(t, s1.NBt, MT), 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int grab = 0;   // thread 0: the sequence index drawn at the start of this tile
+  if (tid == 0) s_next = draw();
+  for (;;) {
+    // every wave is done with the ring; s_next holds the drawn index
+    __syncthreads();
+    if (tid == 0) {
+      // the next position this workgroup owns: a second-product tile, or a
+      // first-product tile nobody has started (else draw again)
+      int k = s_next, c;
+      for (;;) {
+        c = pos_of(k);
+        if (c >= total || c >= total1 || take(c)) break;
+        k = draw();
+      }
+      s_cmd = c;
+      if (c < total) grab = draw();   // the tile after this one
+    }
+    __syncthreads();
+    const int c = uniform(s_cmd);
+    if (c >= total) break;
+    auto drained = [&]() {
+      if (tid == 0) s_next = grab;   // read after the next loop-top barrier
+    };
+    if (c < total1) {
+      first_tile(c, drained);
+      continue;
+    }
+    const int t = c - total1;
+    const int mi = mtile_of(t, s2.NBt, MT);
+    for (;;) {
+      // thread 0: run an unstarted first-product tile of M-tile mi, or wait
+      // for the started ones to finish
+      if (tid == 0) {
+        int steal = -1;
+        if (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < s1.NBt) {
+          for (int nbi = 0; nbi < s1.NBt && steal < 0; ++nbi) {
+            const int t1 = tile_at(mi, nbi, s1.NBt, MT);
+            if (__hip_atomic_load(st + t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+                take(t1))
+              steal = t1;
+          }
+          if (steal < 0) {
+            const unsigned long long t0 = wall_clock64();
+            while (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   s1.NBt) {
+              if (wall_clock64() - t0 > CH_WAIT_TICKS) {   // only when calls share a workspace
+                __hip_atomic_store(ws + CH_ERR, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+        }
+        // acquire: this CU's caches drop lines that may predate the count
+        if (steal < 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_cmd = steal;
+      }
+      __syncthreads();
+      const int steal = uniform(s_cmd);
+      if (steal < 0) break;
+      first_tile(steal, drained);
+      __syncthreads();   // the ring is free again
+    }
+    run_tile<T, FWD2, false, false, false, W>(a2, gl, s2, t, smem, g_idx, drained);
+  }
+  // the last workgroup to finish (every draw and every publish of the
+  // others done) returns the counters to zero for the next call
+  __syncthreads();
+  if (tid == 0)   // release: this workgroup's publishes land before its count
+    s_cmd = __hip_atomic_fetch_add(ws + CH_DONE, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+            nwg - 1;
+  __syncthreads();
+  if (s_cmd) {
+    for (int i = tid; i < MT; i += NT)
+      __hip_atomic_store(dep + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < total1; i += NT)
+      __hip_atomic_store(st + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 8) __hip_atomic_store(ws + CH_XCD + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(ws + CH_DONE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ---------------------------------------------------------------- act recompute
 // act[r, :] = swiglu_act(h13[r, :I], h13[r, I:]) for the rows [lo, hi):
 // the routed window [offsets[g0], offsets[g0+G]) (clamped to R), or [0, n)
@@ -1283,6 +1466,18 @@ int launch_pair(int dt, const GmmArgs& a1, const GmmArgs& a2, hipStream_t s, con
   return moe_check_launch(what);
 }
 
+template <bool GATHER>
+int launch_chain(int dt, const GmmArgs& a1, const GmmArgs& a2, hipStream_t s, const char* what) {
+  constexpr int W = WAVES<bf16_t, FWD1, GATHER>;
+  if (GATHER || dt == MOE_BF16)
+    hipLaunchKernelGGL((gmm_chain_kernel<bf16_t, GATHER, W>), dim3(grid_size()),
+                       dim3(Waves<W>::NT), 0, s, a1, a2);
+  else
+    hipLaunchKernelGGL((gmm_chain_kernel<float, false, 4>), dim3(grid_size()),
+                       dim3(Waves<4>::NT), 0, s, a1, a2);
+  return moe_check_launch(what);
+}
+
 // light: launch the build with the per-fragment-count loops (row-tiled bf16
 // modes), for calls whose groups average at most half a tile of rows
 template <int MODE>
@@ -1339,7 +1534,9 @@ int gmm_checks(const char* fn, const int32_t* offsets, int g0, int G, int R, int
   return MOE_OK;
 }
 
-constexpr size_t WS_BYTES = 256;   // 9 scheduler counters, padded
+// 9 scheduler counters, the forward chain's counters, per-M-tile counters and
+// start words
+constexpr size_t WS_BYTES = (size_t)(CH_ST + CH_MAX_T1) * 4;
 
 // Attach the scheduler workspace (NULL: static tile order).
 int attach_ws(GmmArgs& a, void* ws, size_t ws_bytes, const char* fn) {
@@ -1404,16 +1601,25 @@ int fwd_impl(const char* fn, const void* xp, const int32_t* gather, int gather_r
   a.C = h13; a.ldc = 2 * I;
   a.C2 = act; a.ldc2 = I;
   if (use_sh) { a.sX = sh->x; a.sW = sh->w13; a.sC = sh->h13; a.sC2 = sh->act; }
-  MOE_TRY(launch_dt<FWD1>(dt, a, s, fn, small_groups(a.G, R)));
   // FWD2: yp = act . W2^T (N = H, K = I)
-  a.gather = nullptr;
-  a.N = H; a.K = I;
-  a.X = act; a.ldx = I;
-  a.W = w2; a.ldw = I; a.w_gs = (long long)H * I;
-  a.C = yp; a.ldc = H;
-  a.C2 = nullptr;
-  if (use_sh) { a.sX = sh->act; a.sW = sh->w2; a.sC = sh->y; a.sC2 = nullptr; }
-  return launch_dt<FWD2>(dt, a, s, fn, small_groups(a.G, R));
+  GmmArgs a2 = a;
+  a2.gather = nullptr;
+  a2.N = H; a2.K = I;
+  a2.X = act; a2.ldx = I;
+  a2.W = w2; a2.ldw = I; a2.w_gs = (long long)H * I;
+  a2.C = yp; a2.ldc = H;
+  a2.C2 = nullptr;
+  if (use_sh) { a2.sX = sh->act; a2.sW = sh->w2; a2.sC = sh->y; a2.sC2 = nullptr; }
+  const bool light = small_groups(a.G, R);
+  // one chained launch where the workspace is there, the row tiles fit its
+  // counters (a group adds at most one partial tile) and the groups are not
+  // small ones (their light builds run as two launches)
+  const long long mt_max = ((long long)R + BM - 1) / BM + a.G + ((long long)a.shT + BM - 1) / BM;
+  const long long nb1 = (I + BN / 2 - 1) / (BN / 2);
+  if (a.cnt != nullptr && !light && mt_max <= CH_MAX_MT && mt_max * nb1 <= CH_MAX_T1)
+    return gather ? launch_chain<true>(dt, a, a2, s, fn) : launch_chain<false>(dt, a, a2, s, fn);
+  MOE_TRY(launch_dt<FWD1>(dt, a, s, fn, light));
+  return launch_dt<FWD2>(dt, a2, s, fn, light);
 }
 
 }  // namespace

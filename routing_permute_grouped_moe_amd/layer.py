@@ -10,14 +10,14 @@ Backward: combine bwd -> grouped GEMM dX and dW (one call, paired launches)
           -> route bwd -> router bwd -> permute bwd (which also adds the
           shared expert's and the router's input gradients).
 
-With ``overlap`` (the default on a GPU) the work that does not depend on the
-routing runs on a second stream of the same priority: the shared expert's
-GEMMs (forward: after the router projection, beside route, permute and the
-routed GEMMs; backward: beside everything up to the permute backward) and the
-router backward.  The grouped GEMM draws
-its tiles from per-XCD counters, so whichever kernel holds fewer CUs at the
-end of another one's last round simply takes fewer tiles; results are
-bitwise identical to the sequential order.
+The forward runs on one stream: with the grouped GEMM's workspace, the
+routed and the shared expert's gate/up and down products are one persistent
+launch, which leaves no idle CUs for a second stream to use (a persistent
+GEMM holds every CU it gets, and a GEMM workgroup fills its CU's registers).
+With ``overlap`` the backward runs the route and router backward on a second
+stream of the same priority, beside the grouped GEMM's dX and dW; that
+measured within noise of one stream, so it is off by default.  Results are
+bitwise identical either way.
 
 With ``shape.capacity`` = C the layer is the drop-and-pad variant: every
 expert owns C rows, pairs past an expert's first C (in token order) are
@@ -66,7 +66,7 @@ class LayerShape:
 class MoeLayer:
     """Device buffers of one layer plus the forward/backward call sequences."""
 
-    def __init__(self, shape: LayerShape, device="cuda", overlap: bool = True,
+    def __init__(self, shape: LayerShape, device="cuda", overlap: bool = False,
                  recompute: bool = False):
         s = self.s = shape
         self.overlap = overlap
@@ -110,9 +110,8 @@ class MoeLayer:
         # call leaves them zero); set_gemm_dynamic(False) selects the static order
         self.gws_bytes = abi.moe_gmm_workspace_bytes()
         self.gws = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=dev)
-        self.gws_aux = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=dev)
         self.aux = torch.cuda.Stream(device=dev) if overlap else None
-        self._ev = [torch.cuda.Event() for _ in range(4)] if overlap else None
+        self._ev = [torch.cuda.Event() for _ in range(2)] if overlap else None
         self.h13 = e(R, 2 * I)
         self.act = e(R, I)
         self.yp = z(R, H)            # remote rows stay zero
@@ -146,9 +145,8 @@ class MoeLayer:
         if on:
             self.gws_bytes = abi.moe_gmm_workspace_bytes()
             self.gws = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=self.device)
-            self.gws_aux = torch.zeros(self.gws_bytes, dtype=torch.uint8, device=self.device)
         else:
-            self.gws_bytes, self.gws, self.gws_aux = 0, None, None
+            self.gws_bytes, self.gws = 0, None
 
     def shared_desc(self):
         if not self.s.shared:
@@ -193,19 +191,13 @@ class MoeLayer:
             n += s.R * s.H + s.R * s.I + (s.T * s.I if s.shared else 0)  # xp, act
         return n * b
 
-    def _gmm_sel(self, part):
-        """(G, shared descriptor, workspace) of one grouped-GEMM launch set:
-        part = "all" (routed + shared), "routed" or "shared"."""
-        s = self.s
-        if part == "shared":
-            return 0, self.shared_desc(), self.gws_aux
-        if part == "routed":
-            return s.groups, None, self.gws
-        return s.groups, self.shared_desc(), self.gws
+    def _gmm_sel(self):
+        """(G, shared descriptor, workspace) of the grouped-GEMM calls."""
+        return self.s.groups, self.shared_desc(), self.gws
 
-    def gmm_fwd(self, stream=None, part="all"):
+    def gmm_fwd(self, stream=None):
         s = self.s
-        G, sh, ws = self._gmm_sel(part)
+        G, sh, ws = self._gmm_sel()
         if self.recompute:
             abi.moe_grouped_gemm_fwd_gather(self.x, self.src_token, s.T, self.offsets, s.g0, G,
                                             s.R, self.dt, s.H, s.I, self.w13, self.w2, self.h13,
@@ -228,16 +220,16 @@ class MoeLayer:
         if s.capacity is not None:   # padded rows of dyp: exact zeros through dX and dW
             abi.moe_clear_empty_rows(self.src_token, s.R, self.dt, s.H, self.dyp, stream)
 
-    def gmm_bwd_dx(self, stream=None, part="all"):
+    def gmm_bwd_dx(self, stream=None):
         s = self.s
-        G, sh, ws = self._gmm_sel(part)
+        G, sh, ws = self._gmm_sel()
         abi.moe_grouped_gemm_bwd_dx(self.dyp, self.offsets, s.g0, G, s.R, self.dt, s.H, s.I,
                                     self.w13, self.w2, self.h13, self.dh13, self.dxp, sh, ws,
                                     self.gws_bytes, stream)
 
-    def gmm_bwd_dw(self, stream=None, part="all"):
+    def gmm_bwd_dw(self, stream=None):
         s = self.s
-        G, sh, ws = self._gmm_sel(part)
+        G, sh, ws = self._gmm_sel()
         if self.recompute:
             abi.moe_grouped_gemm_bwd_dw_recompute(self.x, self.src_token, s.T, self.h13, self.act,
                                                   self.dyp, self.dh13, self.offsets, s.g0, G,
@@ -248,15 +240,15 @@ class MoeLayer:
                                     G, s.R, self.dt, s.H, s.I, self.dw13, self.dw2, sh, ws,
                                     self.gws_bytes, stream)
 
-    def gmm_bwd(self, stream=None, part="all"):
+    def gmm_bwd(self, stream=None):
         """dX and dW in one call (paired launches); the recompute variant
         keeps its two calls (dW recomputes act and gathers x)."""
         if self.recompute:
-            self.gmm_bwd_dx(stream, part)
-            self.gmm_bwd_dw(stream, part)
+            self.gmm_bwd_dx(stream)
+            self.gmm_bwd_dw(stream)
             return
         s = self.s
-        G, sh, ws = self._gmm_sel(part)
+        G, sh, ws = self._gmm_sel()
         abi.moe_grouped_gemm_bwd(self.xp, self.act, self.dyp, self.offsets, s.g0, G, s.R, self.dt,
                                  s.H, s.I, self.w13, self.w2, self.h13, self.dh13, self.dxp,
                                  self.dw13, self.dw2, sh, ws, self.gws_bytes, stream)
@@ -284,25 +276,6 @@ class MoeLayer:
 
     def forward(self, stream=None):
         s = self.s
-        if self.overlap and s.shared:
-            main, aux = self._streams(stream)
-            ev_in, ev_sh = self._ev[0], self._ev[1]
-            # the router projection (a GEMM of its own) runs before the fork:
-            # beside the shared expert's GEMMs it only splits the CUs, while
-            # route and permute (latency and HBM bound) fill them in
-            if s.router:
-                self.router_fwd(main)
-            ev_in.record(main)
-            aux.wait_event(ev_in)
-            self.gmm_fwd(aux, part="shared")            # needs x only
-            ev_sh.record(aux)
-            self.route(main)
-            self.permute(main)
-            self.load_stats(main)
-            self.gmm_fwd(main, part="routed")
-            main.wait_event(ev_sh)
-            self.combine(main)
-            return
         if s.router:
             self.router_fwd(stream)
         self.route(stream)
@@ -313,21 +286,16 @@ class MoeLayer:
 
     def backward(self, stream=None):
         s = self.s
-        if self.overlap and (s.shared or s.router):
+        if self.overlap and s.router:
             main, aux = self._streams(stream)
-            ev_in, ev_c, ev_aux = self._ev[0], self._ev[2], self._ev[3]
-            ev_in.record(main)
-            aux.wait_event(ev_in)
-            if s.shared:                                # needs dy and the forward's saves
-                self.gmm_bwd(aux, part="shared")
+            ev_c, ev_aux = self._ev[0], self._ev[1]
             self.combine_bwd(main)
             ev_c.record(main)
             aux.wait_event(ev_c)
             self.route_bwd(aux)                         # needs dgate
-            if s.router:
-                self.router_bwd(aux)
+            self.router_bwd(aux)
             ev_aux.record(aux)
-            self.gmm_bwd(main, part="routed" if s.shared else "all")
+            self.gmm_bwd(main)
             main.wait_event(ev_aux)
             self.permute_bwd(main)
             return

@@ -31,7 +31,7 @@ def shape_of(cfg: MoeConfig, capacity=None):
                       capacity=capacity)
 
 
-def make_layer(cfg: MoeConfig, inp: Inputs, overlap: bool = True, recompute: bool = False,
+def make_layer(cfg: MoeConfig, inp: Inputs, overlap: bool = False, recompute: bool = False,
                capacity=None):
     """A ``MoeLayer`` of ``cfg``'s shape holding ``inp``'s parameters and inputs."""
     import torch

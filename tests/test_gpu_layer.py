@@ -117,11 +117,11 @@ def test_layer_pangu_share_full_size_static_tiles():
 
 
 def test_layer_overlap_matches_sequential_bitwise():
-    # shared expert and router backward on the second stream: same bits as
-    # the one-stream order, over two steps in a row
+    # route and router backward on the second stream: same bits as the
+    # one-stream order, over two steps in a row
     cfg = synth.get_config("pangu")
     inp = synth.make_inputs(cfg)
-    L = make_layer(cfg, inp)
+    L = make_layer(cfg, inp, overlap=True)
     names = ("y", "dx", "dw13", "dw2", "dwg", "dbias", "dws13", "dws2", "dgate")
     res = {}
     for ov in (False, True, True):

@@ -297,6 +297,23 @@ def test_grouped_gemm(abi, counts, H, I, g0, G, shT, dt, dynamic):
     assert rel_err(host(h13), rh13) <= tol
     assert rel_err(host(act), ract) <= tol
     assert rel_err(host(yp), ryp) <= tol
+    if dynamic:
+        # with the workspace both products run in one dependency-ordered
+        # launch (groups above half a tile); without it, as two launches:
+        # the same bits either way
+        s_h13, s_act, s_yp = z(R, 2 * I), z(R, I), z(R, H)
+        ssh = None
+        if shT:
+            sshb = dict(shb, h13=z(shT, 2 * I), act=z(shT, I), y=z(shT, H))
+            ssh = abi.shared_expert(T=shT, **sshb)
+        abi.moe_grouped_gemm_fwd(XP, OFF, g0, G, R, code, H, I, W13, W2, s_h13, s_act, s_yp, ssh,
+                                 None, 0)
+        torch.cuda.synchronize()
+        for name, a, b in (("h13", h13, s_h13), ("act", act, s_act), ("yp", yp, s_yp)):
+            assert torch.equal(a, b), name
+        if shT:
+            for n in ("h13", "act", "y"):
+                assert torch.equal(shb[n], sshb[n]), "shared " + n
     # backward dX / dW on the GPU's own saved activations
     abi.moe_grouped_gemm_bwd_dx(DYP, OFF, g0, G, R, code, H, I, W13, W2, h13, dh13, dxp, sh, ws,
                                 wsb)
