@@ -95,11 +95,18 @@ int moe_router_logits(const void* x, int dt, const float* wg, const float* bias,
  *   dx[T,H]  = dlogits . Wg^T        (written, storage type dt)
  *   dwg[H,E] = x^T . dlogits         (written, fp32)
  *   dbias[E] = sum_t dlogits[t,:]    (written, fp32; nullable)
- * Same workspace as the forward (bf16 dx uses the high bf16 part of each
- * factor only: it is stored in bf16).
+ * Same workspace as the forward.  On the matrix-core path dwg and dbias are
+ * exact to fp32 like the logits; bf16 dx is formed from the high bf16 part
+ * of each factor only (it is stored in bf16: its error stays within a few
+ * bf16 roundings of the exact product).
+ * flags: 0, or MOE_ROUTER_WG_SPLIT: ws still holds the split of this same
+ * wg that moe_router_logits wrote (same T, H, E; workspace not used since),
+ * so the backward skips splitting it again (bits unchanged).  Any other
+ * bit gives MOE_ERR_INVALID_ARG.
  */
+#define MOE_ROUTER_WG_SPLIT 1
 int moe_router_logits_bwd(const float* dlogits, const void* x, int dt, const float* wg,
-                          int T, int H, int E, void* dx, float* dwg, float* dbias,
+                          int T, int H, int E, void* dx, float* dwg, float* dbias, int flags,
                           void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------- routing

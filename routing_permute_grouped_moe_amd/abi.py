@@ -22,6 +22,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUTER_WG_SPLIT = 1          # moe_router_logits_bwd: reuse the forward's split of wg
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 
 _P = ctypes.c_void_p
@@ -48,7 +49,7 @@ _SIGS = {
     "moe_abi_version": (_I, []),
     "moe_router_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moe_router_logits": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _SZ, _P]),
-    "moe_router_logits_bwd": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_router_logits_bwd": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -140,9 +141,9 @@ def moe_router_logits(x, dt, wg, bias, T, H, E, logits, ws=None, ws_bytes=0, str
 
 
 def moe_router_logits_bwd(dlogits, x, dt, wg, T, H, E, dx, dwg, dbias=None, ws=None, ws_bytes=0,
-                          stream=None):
+                          stream=None, flags=0):
     _call("moe_router_logits_bwd", addr(dlogits), addr(x), dt, addr(wg), T, H, E, addr(dx),
-          addr(dwg), addr(dbias), addr(ws), ws_bytes, _stream(stream))
+          addr(dwg), addr(dbias), flags, addr(ws), ws_bytes, _stream(stream))
 
 
 def moe_route(logits, T, E, k, idx, gate, stream=None):

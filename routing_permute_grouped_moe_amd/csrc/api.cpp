@@ -9,7 +9,7 @@
 
 #include "common.hpp"
 
-#define MOE_ABI_VERSION 10
+#define MOE_ABI_VERSION 11
 
 static thread_local char g_last_error[512];
 

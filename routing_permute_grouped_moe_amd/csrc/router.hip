@@ -304,9 +304,11 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
     const RouterWs L = router_ws_layout(T, H, E);
     char* w = (char*)ws;
     bf16_t* wg3s = (bf16_t*)(w + L.wg3s);
+    bf16_t* wgb = (bf16_t*)(w + L.wgb);
     float* part = (float*)(w + L.part);
+    // the hi parts too: the backward can reuse this split (MOE_ROUTER_WG_SPLIT)
     hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
-                       wg3s, (bf16_t*)nullptr);
+                       wg3s, wgb);
     MOE_TRY(moe_check_launch(fn));
     MOE_TRY(moe_gmm_router_fwd(x, wg3s, part, T, H, E, RT_SPLIT, s));
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s,
@@ -322,9 +324,11 @@ extern "C" int moe_router_logits(const void* x, int dt, const float* wg, const f
 
 extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt, const float* wg,
                                      int T, int H, int E, void* dx, float* dwg, float* dbias,
-                                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+                                     int flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
   const char* fn = "moe_router_logits_bwd";
   MOE_TRY(router_checks(fn, dt, T, H, E));
+  if (flags & ~MOE_ROUTER_WG_SPLIT)
+    return moe_fail(MOE_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
   MOE_TRY(moe_need_ptr(dwg, fn, "dwg", 4));
   MOE_TRY(moe_opt_ptr(dbias, fn, "dbias", 4));
   hipStream_t s = (hipStream_t)stream;
@@ -361,9 +365,11 @@ extern "C" int moe_router_logits_bwd(const float* dlogits, const void* x, int dt
     float* part = (float*)(w + L.part);
     bf16_t* dl3s = (bf16_t*)(w + L.dl3s);
     bf16_t* dlb = (bf16_t*)(w + L.dlb);
-    hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H, E,
-                       wg3s, wgb);
-    MOE_TRY(moe_check_launch(fn));
+    if (!(flags & MOE_ROUTER_WG_SPLIT)) {
+      hipLaunchKernelGGL(split_wg_kernel, dim3(grid_for((long long)H * E)), dim3(256), 0, s, wg, H,
+                         E, wg3s, wgb);
+      MOE_TRY(moe_check_launch(fn));
+    }
     hipLaunchKernelGGL(split_dl_kernel, dim3(grid_for((long long)T * E)), dim3(256), 0, s, dlogits,
                        T, E, dl3s, dlb);
     MOE_TRY(moe_check_launch(fn));

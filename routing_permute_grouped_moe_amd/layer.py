@@ -106,6 +106,7 @@ class MoeLayer:
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         self.rws_bytes = abi.moe_router_workspace_bytes(T, H, E, self.dt) if s.router else 0
         self.rws = torch.empty(max(self.rws_bytes, 256), dtype=torch.uint8, device=dev)
+        self._wg_split = False
         # tile scheduler counters of the grouped GEMM (zero-filled once; every
         # call leaves them zero); set_gemm_dynamic(False) selects the static order
         self.gws_bytes = abi.moe_gmm_workspace_bytes()
@@ -161,6 +162,7 @@ class MoeLayer:
         s = self.s
         abi.moe_router_logits(self.x, self.dt, self.wg, self.bias, s.T, s.H, s.E, self.logits,
                               self.rws, self.rws_bytes, stream)
+        self._wg_split = True    # the router workspace now holds wg's split
 
     def route(self, stream=None):
         s = self.s
@@ -258,10 +260,13 @@ class MoeLayer:
         abi.moe_route_bwd(self.logits, self.idx, self.dgate, s.T, s.E, s.k, self.dlogits, stream)
 
     def router_bwd(self, stream=None):
+        """Reuses the split of wg that router_fwd left in the router
+        workspace (the step order: wg does not change between the two)."""
         s = self.s
+        flags = abi.MOE_ROUTER_WG_SPLIT if self._wg_split else 0
         abi.moe_router_logits_bwd(self.dlogits, self.x, self.dt, self.wg, s.T, s.H, s.E,
                                   self.dx_router, self.dwg, self.dbias, self.rws, self.rws_bytes,
-                                  stream)
+                                  stream, flags=flags)
 
     def permute_bwd(self, stream=None):
         s = self.s

@@ -176,3 +176,10 @@ def test_noalloc_permute_size_limit(abi):
     st = status(abi, "moe_permute_noalloc", FAKE, 1, FAKE, 100, 100, 8, 2, FAKE, FAKE, FAKE,
                 FAKE, FAKE, None)
     assert st == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_router_bwd_rejects_unknown_flags(abi):
+    # dlogits, x, dt, wg, T, H, E, dx, dwg, dbias, flags, ws, ws_bytes, stream
+    args = [FAKE, FAKE, abi.MOE_BF16, FAKE, 512, 256, 64, FAKE, FAKE, None, 2, FAKE, 1 << 30, None]
+    assert status(abi, "moe_router_logits_bwd", *args) == abi.MOE_ERR_INVALID_ARG
+    assert "flags" in abi.moe_last_error()

@@ -150,10 +150,12 @@ def test_layer_full_size_sampled(name):
         rep["dbias"] = rel_err(host(L.dbias), db_ref)
         assert rep["dwg"] <= 1e-5 and rep["dbias"] <= 1e-5
 
-    # ---- whole weight gradients of two small groups; empty groups exactly zero
+    # ---- whole weight gradients of the smallest, a ~100-row and the largest
+    # group; empty groups exactly zero
     small = int(nonempty[np.argmin(counts[nonempty])])
     mid = int(nonempty[np.argmin(np.abs(counts[nonempty] - 100))])
-    for e in sorted({small, mid}):
+    large = int(nonempty[np.argmax(counts[nonempty])])
+    for e in sorted({small, mid, large}):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         r = np.arange(lo, hi)
         t_of = src[r]

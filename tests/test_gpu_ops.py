@@ -220,11 +220,25 @@ def test_router_projection(abi, T, H, E, dt):
     dx = torch.empty(T, H, dtype=tdt, device="cuda")
     dwg = torch.empty(H, E, dtype=torch.float32, device="cuda")
     db = torch.empty(E, dtype=torch.float32, device="cuda")
-    abi.moe_router_logits_bwd(dev(dl, torch.float32), X, _code(abi, dt), WG, T, H, E, dx, dwg, db,
-                              ws, wsb)
+    DL = dev(dl, torch.float32)
+    # right after the forward the workspace still holds wg's split: reusing
+    # it gives the same bits
+    abi.moe_router_logits_bwd(DL, X, _code(abi, dt), WG, T, H, E, dx, dwg, db, ws, wsb,
+                              flags=abi.MOE_ROUTER_WG_SPLIT)
+    dx2, dwg2, db2 = torch.empty_like(dx), torch.empty_like(dwg), torch.empty_like(db)
+    abi.moe_router_logits_bwd(DL, X, _code(abi, dt), WG, T, H, E, dx2, dwg2, db2, ws, wsb)
     torch.cuda.synchronize()
+    assert torch.equal(dx, dx2) and torch.equal(dwg, dwg2) and torch.equal(db, db2)
     rdx, rdwg, rdb = oracle.router_backward(dl, x, wg)
-    assert rel_err(host(dx), rdx) <= TOL[dt]
+    err_dx = rel_err(host(dx), rdx)
+    assert err_dx <= TOL[dt]
+    if dt == "bf16":
+        # dx from the bf16 high parts of dlogits and wg, stored in bf16: its
+        # error stays within a few times that of storing the exact product
+        # in bf16 (the output rounding alone)
+        err_store = rel_err(synth.bf16_round(rdx.astype(np.float32)), rdx)
+        print(f"router dx: error {err_dx:.2e}, bf16 storage alone {err_store:.2e}")
+        assert err_dx <= 3 * err_store
     assert rel_err(host(dwg), rdwg) <= 1e-5
     assert rel_err(host(db), rdb) <= 1e-5
 
