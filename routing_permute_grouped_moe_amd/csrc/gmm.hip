@@ -45,17 +45,22 @@ constexpr int BM = 256, BN = 256;
 constexpr int WTM = 128;             // wave tile rows (two wave rows per tile)
 constexpr int FM = 4;                // 32-row fragments per wave tile
 
-// W wavefronts per workgroup: 2 wave rows x W/2 wave columns.  W = 4 gives
-// each wave a 128 x 128 tile (4 x 4 fragments, accumulators in the AGPRs,
-// one wave per SIMD); W = 8 gives 128 x 64 (4 x 2 fragments, two waves per
-// SIMD, so one wave's MFMAs run while the other waits on LDS or a barrier).
-template <int W>
+// W wavefronts per workgroup in WM wave rows x W/WM wave columns over a
+// tile of WM * 128 rows and 256 columns.  W = 4, WM = 2 gives each wave a
+// 128 x 128 tile (4 x 4 fragments, accumulators in the AGPRs, one wave per
+// SIMD); W = 8 gives 128 x 64 (4 x 2 fragments, two waves per SIMD, so one
+// wave's MFMAs run while the other waits on LDS or a barrier).  W = 4,
+// WM = 1 is the strip tile for row tiles of at most 128 rows: one row of
+// four 128 x 64 waves, so a short row tile costs half a tile, not a whole
+// one with two waves on padding.
+template <int W, int WM = 2>
 struct Waves {
-  static constexpr int NT = 64 * W;    // threads per workgroup
-  static constexpr int WN = W / 2;     // wave columns
-  static constexpr int FN = 16 / W;    // 32-column fragments per wave tile
-  static constexpr int WTN = 32 * FN;  // wave tile columns
-  static constexpr int HW = WTN / 2;   // a wave's columns in one epilogue slice
+  static constexpr int NT = 64 * W;       // threads per workgroup
+  static constexpr int WN = W / WM;       // wave columns
+  static constexpr int FN = 8 / WN;       // 32-column fragments per wave tile
+  static constexpr int WTN = 32 * FN;     // wave tile columns
+  static constexpr int HW = WTN / 2;      // a wave's columns in one epilogue slice
+  static constexpr int BMT = WM * 128;    // tile rows
 };
 constexpr int RING_BYTES = 131072;   // LDS ring of operand stages (also the epilogue slice)
 constexpr int GM_BAND = 8;           // M-tiles per band in the tile order
@@ -202,11 +207,10 @@ __device__ __forceinline__ View make_view(const void* base, long long bytes, int
 //
 // K-major: a copy covers 1024 / ROWB whole rows; lane l fills row
 // q * RPC + l / LPR, slot l % LPR, from the chunk that belongs in that slot.
-template <typename T, bool SWIGLU, int W>
+template <typename T, bool SWIGLU, int WTN, int DPO>
 __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
-                                               uint32_t (&off)[DPO_OF<T, W>]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
-  constexpr int WTN = Waves<W>::WTN, HW = Waves<W>::HW;
+                                               uint32_t (&off)[DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, HW = WTN / 2;
   constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;   // lanes per row, rows per copy
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -234,10 +238,9 @@ __device__ __forceinline__ void kmajor_offsets(const View& v, int mn0, int I,
 
 // MN-major: bf16 copy q covers K rows 2q, 2q+1 (lane l: row 2q + l/32, slot
 // l%32); fp32 copy q covers K row q (lane l: slot l).
-template <typename T, int W>
-__device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
-                                                uint32_t (&off)[DPO_OF<T, W>]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
+template <typename T, int DPO>
+__device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0, uint32_t (&off)[DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < DPO; ++j) {
@@ -257,11 +260,10 @@ __device__ __forceinline__ void mnmajor_offsets(const View& v, int mn0,
 
 // K-major, rows gathered: tile row `row` (< rows) is row gather[rows0 + row]
 // of the view; the indices are read once per tile.
-template <typename T, int W>
+template <typename T, int DPO>
 __device__ __forceinline__ void kmajor_offsets_gather(const View& v, const int32_t* gather,
-                                                      int rows0, int rows,
-                                                      uint32_t (&off)[DPO_OF<T, W>]) {
-  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC, DPO = DPO_OF<T, W>;
+                                                      int rows0, int rows, uint32_t (&off)[DPO]) {
+  constexpr int ES = Cfg<T>::ES, VEC = Cfg<T>::VEC;
   constexpr int LPR = Cfg<T>::ROWB / 16, RPC = 64 / LPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t gi = make_rsrc(gather + rows0, (uint32_t)rows * 4u);
@@ -337,9 +339,9 @@ __device__ __forceinline__ auto read_frag(const char* lds, int r0, int ks) {
 // n = 32 j + 8 (r/4) + 4 (lane/32) + r%4: every lane owns runs of four
 // consecutive output columns, which the epilogue writes to LDS as one
 // 16-byte store.
-template <typename T, bool A_MN, bool B_MN, int W>
+template <typename T, bool A_MN, bool B_MN, int W, int WM>
 struct Frags {
-  static constexpr int FN = Waves<W>::FN, WTN = Waves<W>::WTN;
+  static constexpr int FN = Waves<W, WM>::FN, WTN = Waves<W, WM>::WTN;
   decltype(read_frag<T, A_MN>(nullptr, 0, 0)) a[FM];
   decltype(read_frag<T, B_MN>(nullptr, 0, 0)) b[FN];
   __device__ __forceinline__ void load(const char* la, const char* lb, int wm, int wn, int ks) {
@@ -494,15 +496,44 @@ __device__ __forceinline__ Space tile_space(const GmmArgs& a, const GroupLds& gl
 }
 
 // ---------------------------------------------------------------- one tile
+// Row tile tile_id of a row-tiled product: group g, rows [rows0, rows0 +
+// rows) (rows <= BM) and N-tile nbi, in band order: GM_BAND M-tiles at a
+// time, every N-tile of them, M fastest.
+struct RowTile {
+  int g, rows0, rows, nbi;
+};
+__device__ __forceinline__ RowTile locate_row_tile(const GroupLds& gl, const Space& sp, int ng,
+                                                   int tile) {
+  const int MT = gl.pre[ng];
+  const int band = GM_BAND * sp.NBt;
+  const int sup = tile / band, within = tile % band;
+  const int first = sup * GM_BAND;
+  const int gsz = min(GM_BAND, MT - first);
+  const int mi = first + within % gsz;
+  RowTile rt;
+  rt.nbi = within / gsz;
+  // group of M-tile mi: last g with pre[g] <= mi and a non-empty range
+  int lo = 0, hi = ng - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gl.pre[mid] <= mi) lo = mid; else hi = mid - 1;
+  }
+  rt.g = lo;
+  rt.rows0 = gl.lo[lo] + (mi - gl.pre[lo]) * BM;
+  rt.rows = min(BM, gl.hi[lo] - rt.rows0);
+  return rt;
+}
+
 // Tile tile_id of a product: main loop over K and epilogue.  smem is the
 // 128 KB operand ring (also the epilogue's staging), g_idx the gathered-row
 // index ring.  drained() runs once per tile, by every thread, at the point
 // where every copy of the tile and the scheduler's draw have landed.
 template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, bool ACT_DEV = false,
-          typename Drained>
+          int WM = 2, typename Drained>
 __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
                                          int tile_id, char* smem, int* g_idx, Drained&& drained) {
-  constexpr int NT = Waves<W>::NT, WN = Waves<W>::WN, FN = Waves<W>::FN, HW = Waves<W>::HW;
+  using WS = Waves<W, WM>;
+  constexpr int NT = WS::NT, WN = WS::WN, FN = WS::FN, HW = WS::HW, BMT = WS::BMT;
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
   // DW with gathered Q rows: the rows change every K step, so each wave also
   // copies its K rows' indices into an LDS ring, two steps before the copies
@@ -517,36 +548,33 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
   constexpr int STAGES = Cfg<T>::STAGES, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
-  constexpr int DMA_PER_OP = DPO_OF<T, W>;
-  constexpr int DMA_PER_STEP = 2 * DMA_PER_OP;   // buffer loads per wave per K step
+  static_assert(WM == 2 || (WM == 1 && W == 4 && sizeof(T) == 2 && MODE != DW && !LIGHT),
+                "strip tiles: bf16 row-tiled products, 4 waves");
+  // buffer loads per wave per K step: DPA for the A tile (BMT rows), DPB for
+  // the B tile (256 rows or columns)
+  constexpr int DPB = DPO_OF<T, W>;
+  constexpr int DPA = DPB * WM / 2;
+  constexpr int DMA_PER_STEP = DPA + DPB;
+  // MFMA slots of a half K step that issue the A (first half) and B (second
+  // half) copies: right after the fragment loads, or the last slots where
+  // a half step has fewer MFMAs than loads and copies
+  constexpr int CS1 = (FM + FN < FM * FN - DPA) ? FM + FN : FM * FN - DPA;
+  constexpr int CS2 = (FM + FN < FM * FN - DPB) ? FM + FN : FM * FN - DPB;
   static_assert(STAGES * STAGE_BYTES == RING_BYTES, "stage ring size");
   static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;   // 2 x WN wave grid
+  const int wm = wave / WN, wn = wave % WN;   // WM x WN wave grid
   const int ng = a.G + a.shared;
   // ---- locate the tile
   int g, m0, n0, rows0 = 0, rows = 0, kdim;
   if constexpr (MODE != DW) {
-    const int tile = tile_id;
-    const int MT = gl.pre[ng];
-    const int band = GM_BAND * sp.NBt;
-    const int sup = tile / band, within = tile % band;
-    const int first = sup * GM_BAND;
-    const int gsz = min(GM_BAND, MT - first);
-    const int mi = first + within % gsz;
-    const int nbi = within / gsz;
-    // group of M-tile mi: last g with pre[g] <= mi and a non-empty range
-    int lo = 0, hi = ng - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (gl.pre[mid] <= mi) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-    rows0 = gl.lo[g] + (mi - gl.pre[g]) * BM;
-    rows = min(BM, gl.hi[g] - rows0);
+    const RowTile rt = locate_row_tile(gl, sp, ng, tile_id);
+    g = rt.g;
+    rows0 = rt.rows0;
+    rows = rt.rows;
     m0 = 0;
-    n0 = nbi * ((MODE == FWD1) ? BN / 2 : BN);
+    n0 = rt.nbi * ((MODE == FWD1) ? BN / 2 : BN);
     kdim = a.K;
   } else {
     const int per = sp.MBt * sp.NBt;   // tiles of one group
@@ -602,19 +630,19 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = (kdim + BK - 1) / BK;   // K steps with data
-  uint32_t offa[DMA_PER_OP], offb[DMA_PER_OP];
-  if constexpr (A_MN) mnmajor_offsets<T, W>(va, m0, offa);
+  uint32_t offa[DPA], offb[DPB];
+  if constexpr (A_MN) mnmajor_offsets<T>(va, m0, offa);
   else if (GATHER && MODE == FWD1 && gat)
-    kmajor_offsets_gather<T, W>(va, a.gather, rows0, rows, offa);
-  else kmajor_offsets<T, false, W>(va, m0, 0, offa);
+    kmajor_offsets_gather<T>(va, a.gather, rows0, rows, offa);
+  else kmajor_offsets<T, false, WS::WTN>(va, m0, 0, offa);
   if constexpr (GLOOP) {
     // gathered Q: only the column part is fixed; the row part comes with
     // each K step's indices (view with ld 0 gives column offsets)
     View vc = vb;
     if (gat) vc.ld = 0;
-    mnmajor_offsets<T, W>(vc, n0, offb);
-  } else if constexpr (B_MN) mnmajor_offsets<T, W>(vb, n0, offb);
-  else kmajor_offsets<T, MODE == FWD1, W>(vb, n0, a.I, offb);
+    mnmajor_offsets<T>(vc, n0, offb);
+  } else if constexpr (B_MN) mnmajor_offsets<T>(vb, n0, offb);
+  else kmajor_offsets<T, MODE == FWD1, WS::WTN>(vb, n0, a.I, offb);
   const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
   const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
   const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
@@ -623,22 +651,22 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     issue_op(va, st, offa, (kt % wrap_steps) * sa);
     issue_op(vb, st + OPB, offb, kt * sb);
   };
-  // copy j of K step kt (j < DMA_PER_OP: operand A, else B); a step past the
+  // copy j of K step kt (j < DPA: operand A, else B); a step past the
   // last one copies through an empty descriptor, which moves no HBM bytes
   // and only writes zeros into a stage nobody reads
   const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
-  const uint32_t lds_w = lds_addr(smem) + (threadIdx.x >> 6) * DMA_PER_OP * 1024;
+  const uint32_t lds_wa = lds_addr(smem) + (threadIdx.x >> 6) * DPA * 1024;
+  const uint32_t lds_wb = lds_addr(smem) + OPB + (threadIdx.x >> 6) * DPB * 1024;
   // (the A step index wraps for dW tiles that re-read a short operand;
   // ka_next tracks kt % wrap_steps of the next step to issue)
   int ka_next = 0;
   auto issue1 = [&](int kt, int j) {
-    const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
     const bool live = kt < KT;
-    if (j < DMA_PER_OP)
-      dma16(live ? va.rs : rs_none, st + j * 1024, offa[j], ka_next * sa);
+    if (j < DPA)
+      dma16(live ? va.rs : rs_none, lds_wa + so + j * 1024, offa[j], ka_next * sa);
     else
-      dma16(live ? vb.rs : rs_none, st + OPB + (j - DMA_PER_OP) * 1024, offb[j - DMA_PER_OP],
-            kt * sb);
+      dma16(live ? vb.rs : rs_none, lds_wb + so + (j - DPA) * 1024, offb[j - DPA], kt * sb);
     if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
   };
   auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
@@ -664,12 +692,12 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     return *(const u32x4*)(g_idx + (wave * 4 + (kt & 3)) * 64 + 4 * hrow);
   };
   auto issue_b = [&](int kt, int j, const u32x4& iv) {
-    const uint32_t st = lds_w + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
     const int krow = kt * BK + 8 * wave + 2 * j + hrow;
     const uint32_t vo =
         gat ? ((krow < kdim && offb[j] != OOB) ? iv[j] * rowb + offb[j] : OOB) : offb[j];
-    dma16(kt < KT ? vb.rs : rs_none, st + OPB + j * 1024, vo, kt * sb);
-    if (j == DMA_PER_OP - 1 && ++ka_next == wrap_steps) ka_next = 0;
+    dma16(kt < KT ? vb.rs : rs_none, lds_wb + so + j * 1024, vo, kt * sb);
+    if (j == DPB - 1 && ++ka_next == wrap_steps) ka_next = 0;
   };
 
   if (KT > 0) {
@@ -688,9 +716,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
 #pragma unroll
         for (int kt = 0; kt < STAGES - 1; ++kt) {
 #pragma unroll
-          for (int j = 0; j < DMA_PER_OP; ++j) issue1(kt, j);
+          for (int j = 0; j < DPA; ++j) issue1(kt, j);
 #pragma unroll
-          for (int j = 0; j < DMA_PER_OP; ++j) issue_b(kt, j, iv[kt]);
+          for (int j = 0; j < DPB; ++j) issue_b(kt, j, iv[kt]);
           if (kt >= 1) issue_idx(kt + 2);
         }
       } else {
@@ -730,7 +758,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
         constexpr int FA = decltype(fa_c)::value;
         // fragment q of a load (q < FM: A fragment q, else B fragment q - FM)
         auto need = [](int q) { return q < FM ? q < FA : FA > 0; };
-        Frags<T, A_MN, B_MN, W> f0, f1;
+        Frags<T, A_MN, B_MN, W, WM> f0, f1;
 #pragma unroll
         for (int q = 0; q < FM + FN; ++q)
           if (need(q)) f0.load1(stage(0), stage(0) + OPB, wm, wn, 0, q);
@@ -744,14 +772,11 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               const int q = i * FN + j;
               if (i < FA) acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
-              if (q < FM + FN) {
-                if (need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-              } else if (q - (FM + FN) < DMA_PER_OP) {
-                issue1(kt + STAGES - 1, q - (FM + FN));
-              }
+              if (q < FM + FN && need(q)) f1.load1(cs, cs + OPB, wm, wn, 1, q);
+              if (q >= CS1 && q - CS1 < DPA) issue1(kt + STAGES - 1, q - CS1);
               __builtin_amdgcn_sched_barrier(0);
             }
-          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+          wait_vm<DMA_PER_STEP + DPA + GI>();
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -760,11 +785,8 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               const int q = i * FN + j;
               if (i < FA) acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
-              if (q < FM + FN) {
-                if (need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-              } else if (q - (FM + FN) < DMA_PER_OP) {
-                issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-              }
+              if (q < FM + FN && need(q)) f0.load1(ns, ns + OPB, wm, wn, 0, q);
+              if (q >= CS2 && q - CS2 < DPB) issue1(kt + STAGES - 1, DPA + q - CS2);
               __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -780,7 +802,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           default: kloop(std::integral_constant<int, FM>{}); break;
         }
       } else {
-        Frags<T, A_MN, B_MN, W> f0, f1;
+        Frags<T, A_MN, B_MN, W, WM> f0, f1;
         f0.load(stage(0), stage(0) + OPB, wm, wn, 0);
         for (int kt = 0; kt < KT; ++kt) {
           const char* cs = stage(kt);
@@ -793,7 +815,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               acc[i][j] = mfma_step(f0.b[j], f0.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
               if (q < FM + FN) f1.load1(cs, cs + OPB, wm, wn, 1, q);
-              else if (q - (FM + FN) < DMA_PER_OP) issue1(kt + STAGES - 1, q - (FM + FN));
+              if (q >= CS1 && q - CS1 < DPA) issue1(kt + STAGES - 1, q - CS1);
               __builtin_amdgcn_sched_barrier(0);
             }
           // K step kt+1 has landed once at most the copies issued after it
@@ -802,7 +824,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           // stage refilled next
           // (GLOOP: also step kt+3's indices, issued right after step
           // kt+1's B copies, and one index copy more per step since)
-          wait_vm<DMA_PER_STEP + DMA_PER_OP + GI>();
+          wait_vm<DMA_PER_STEP + DPA + GI>();
           __syncthreads();
           u32x4 ivn;
           if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
@@ -814,10 +836,10 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               acc[i][j] = mfma_step(f1.b[j], f1.a[i], acc[i][j]);
               __builtin_amdgcn_sched_barrier(0);
               if (q < FM + FN) f0.load1(ns, ns + OPB, wm, wn, 0, q);
-              else if (q - (FM + FN) < DMA_PER_OP) {
-                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - (FM + FN), ivn);
-                else issue1(kt + STAGES - 1, DMA_PER_OP + q - (FM + FN));
-              } else if (GLOOP && q == FM + FN + DMA_PER_OP) {
+              if (q >= CS2 && q - CS2 < DPB) {
+                if constexpr (GLOOP) issue_b(kt + STAGES - 1, q - CS2, ivn);
+                else issue1(kt + STAGES - 1, DPA + q - CS2);
+              } else if (GLOOP && q == CS2 + DPB) {
                 issue_idx(kt + STAGES + 1);
               }
               __builtin_amdgcn_sched_barrier(0);
@@ -825,7 +847,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
         }
       }
     } else {
-      Frags<T, A_MN, B_MN, W> cur, nxt;
+      Frags<T, A_MN, B_MN, W, WM> cur, nxt;
       cur.load(stage(0), stage(0) + OPB, wm, wn, 0);
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -887,9 +909,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     __syncthreads();
   };
   auto take = [&](auto&& consume) {
-    // 256 rows x 16 chunks of 8 columns, 4096 / NT per thread
+    // BMT rows x 16 chunks of 8 columns, BMT * 16 / NT per thread
 #pragma unroll 4
-    for (int it = 0; it < 4096 / NT; ++it) {
+    for (int it = 0; it < BMT * 16 / NT; ++it) {
       const int idx = it * NT + etid;
       const int row = idx >> 4, cc = (idx & 15) * 8;
       const int sw = row & 31;
@@ -1020,7 +1042,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           store8(dr, ok, (uint32_t)(row * a.ldc + a.I + i), du);
         };
         if (sizeof(T) == 2) {
-          // bf16: the slice's gate/up chunks (4096 / NT per thread) are
+          // bf16: the slice's gate/up chunks (BMT * 16 / NT per thread) are
           // requested before the accumulators are staged, so their latency
           // hides behind the LDS round trip instead of serializing with the
           // stores (a load may not pass an earlier store to a buffer that
@@ -1028,7 +1050,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           // half is requested after the first half's stores), which keeps a
           // kernel that also holds another product's code within the
           // register file
-          constexpr int CH = 4096 / NT;          // chunks per thread
+          constexpr int CH = BMT * 16 / NT;      // chunks per thread
           constexpr int PF = LEAN ? CH / 2 : CH;
           u32x4 graw[PF], uraw[PF];
           auto fetch = [&](int it) {
@@ -1127,6 +1149,26 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   }
 }
 
+// A row tile of at most 128 rows runs as a strip tile (bf16, 4 waves):
+// half the copies and MFMAs of a full tile, the same bits.
+template <typename T, int MODE, bool GATHER, bool LEAN, int W, bool ACT_DEV = false,
+          typename Drained>
+__device__ __forceinline__ void run_row_tile(const GmmArgs& a, const GroupLds& gl,
+                                             const Space& sp, int tile_id, char* smem,
+                                             int* g_idx, Drained&& drained) {
+  static_assert(MODE != DW, "row-tiled products");
+  if constexpr (sizeof(T) == 2 && W == 4) {
+    if (uniform(locate_row_tile(gl, sp, a.G + a.shared, tile_id).rows) <= WTM) {
+      // (LEAN: the strip's epilogue holds fewer prefetched chunks, so the
+      // kernel that also holds the full tile's code stays in its registers)
+      run_tile<T, MODE, GATHER, false, true, W, ACT_DEV, 1>(a, gl, sp, tile_id, smem, g_idx,
+                                                           drained);
+      return;
+    }
+  }
+  run_tile<T, MODE, GATHER, false, LEAN, W, ACT_DEV, 2>(a, gl, sp, tile_id, smem, g_idx, drained);
+}
+
 // ---------------------------------------------------------------- the kernels
 // Persistent tile loop.  Tiles are dealt in rounds of one per workgroup; in
 // each round the workgroups of XCD x (workgroup i runs on XCD i % 8) take the
@@ -1194,7 +1236,10 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
   else group_order(ng, gl);
   const Space sp = tile_space<MODE, LIGHT>(a, gl, &s_next);
   persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained) {
-    run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained);
+    if constexpr (MODE != DW && !LIGHT)   // (DX1 lean: both tile shapes fit the registers)
+      run_row_tile<T, MODE, GATHER, MODE == DX1, W>(a, gl, sp, n, smem, g_idx, drained);
+    else
+      run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained);
   });
 }
 
@@ -1223,7 +1268,7 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, G
   const int splitA = lead * s2.MBt * s2.NBt;
   persistent_loop(a1.cnt, s1.total + s2.total, &s_next, [&](int n, auto&& drained) {
     if (n >= splitA && n < splitA + s1.total)
-      run_tile<T, M1, false, false, true, W>(a1, gl, s1, n - splitA, smem, g_idx, drained);
+      run_row_tile<T, M1, false, true, W>(a1, gl, s1, n - splitA, smem, g_idx, drained);
     else
       run_tile<T, M2, false, false, true, W>(a2, gl, s2, n < splitA ? n : n - s1.total, smem,
                                              g_idx, drained);
@@ -1303,8 +1348,78 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_chain_kernel(GmmArgs a1, 
   auto take = [&](int t) {   // thread 0: start first-product tile t unless started
     return __hip_atomic_exchange(st + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
   };
-  auto first_tile = [&](int t, auto&& drained) {
-    run_tile<T, FWD1, GATHER, false, false, W, true>(a1, gl, s1, t, smem, g_idx, drained);
+  int grab = 0;   // thread 0: the sequence index drawn for the claim after this one
+  int pend = -1;  // thread 0: a claimed second-product position still waiting
+  if (tid == 0) s_next = draw();
+  for (;;) {
+    // every wave is done with the ring; s_next holds the drawn index
+    __syncthreads();
+    if (tid == 0) {
+      // what this workgroup runs next (s_cmd): a first-product tile it owns
+      // (claimed, or unstarted and needed by its waiting second-product
+      // tile), a second-product tile whose row tile is done, or total: done
+      int cmd = total;
+      for (;;) {
+        if (pend < 0) {
+          // claim: a second-product position, or a first-product tile
+          // nobody has started (else draw again)
+          int k = s_next, c;
+          for (;;) {
+            c = pos_of(k);
+            if (c >= total || c >= total1 || take(c)) break;
+            k = draw();
+          }
+          if (c >= total) break;
+          grab = draw();   // the claim after this one
+          if (c < total1) {
+            cmd = c;
+            break;
+          }
+          pend = c;
+        }
+        const int mi = mtile_of(pend - total1, s2.NBt, MT);
+        if (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < s1.NBt) {
+          int steal = -1;
+          for (int nbi = 0; nbi < s1.NBt && steal < 0; ++nbi) {
+            const int t1 = tile_at(mi, nbi, s1.NBt, MT);
+            if (__hip_atomic_load(st + t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+                take(t1))
+              steal = t1;
+          }
+          if (steal >= 0) {   // run it now; the second-product tile stays pending
+            cmd = steal;
+            break;
+          }
+          // every first-product tile of the row tile is running elsewhere
+          const unsigned long long t0 = wall_clock64();
+          while (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                 s1.NBt) {
+            if (wall_clock64() - t0 > CH_WAIT_TICKS) {   // only when calls share a workspace
+              __hip_atomic_store(ws + CH_ERR, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        // acquire: this CU's caches drop lines that may predate the count
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        cmd = pend;
+        pend = -1;
+        break;
+      }
+      s_cmd = cmd;
+    }
+    __syncthreads();
+    const int c = uniform(s_cmd);
+    if (c >= total) break;
+    auto drained = [&]() {
+      if (tid == 0) s_next = grab;   // read after the next loop-top barrier
+    };
+    if (c >= total1) {
+      run_row_tile<T, FWD2, false, false, W>(a2, gl, s2, c - total1, smem, g_idx, drained);
+      continue;
+    }
+    run_row_tile<T, FWD1, GATHER, false, W, true>(a1, gl, s1, c, smem, g_idx, drained);
     // publish: the act rows were stored at device scope (write-through), so
     // once every wave's stores have completed the count can go out -- the
     // compiler's agent-scope release for such stores is this same wait.  (A
@@ -1314,73 +1429,8 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_chain_kernel(GmmArgs a1, 
     wait_vm<0>();
     __syncthreads();
     if (tid == 0)
-      __hip_atomic_fetch_add(dep + mtile_of(t, s1.NBt, MT), 1, __ATOMIC_RELAXED,
+      __hip_atomic_fetch_add(dep + mtile_of(c, s1.NBt, MT), 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-  };
-  int grab = 0;   // thread 0: the sequence index drawn at the start of this tile
-  if (tid == 0) s_next = draw();
-  for (;;) {
-    // every wave is done with the ring; s_next holds the drawn index
-    __syncthreads();
-    if (tid == 0) {
-      // the next position this workgroup owns: a second-product tile, or a
-      // first-product tile nobody has started (else draw again)
-      int k = s_next, c;
-      for (;;) {
-        c = pos_of(k);
-        if (c >= total || c >= total1 || take(c)) break;
-        k = draw();
-      }
-      s_cmd = c;
-      if (c < total) grab = draw();   // the tile after this one
-    }
-    __syncthreads();
-    const int c = uniform(s_cmd);
-    if (c >= total) break;
-    auto drained = [&]() {
-      if (tid == 0) s_next = grab;   // read after the next loop-top barrier
-    };
-    if (c < total1) {
-      first_tile(c, drained);
-      continue;
-    }
-    const int t = c - total1;
-    const int mi = mtile_of(t, s2.NBt, MT);
-    for (;;) {
-      // thread 0: run an unstarted first-product tile of M-tile mi, or wait
-      // for the started ones to finish
-      if (tid == 0) {
-        int steal = -1;
-        if (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < s1.NBt) {
-          for (int nbi = 0; nbi < s1.NBt && steal < 0; ++nbi) {
-            const int t1 = tile_at(mi, nbi, s1.NBt, MT);
-            if (__hip_atomic_load(st + t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
-                take(t1))
-              steal = t1;
-          }
-          if (steal < 0) {
-            const unsigned long long t0 = wall_clock64();
-            while (__hip_atomic_load(dep + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                   s1.NBt) {
-              if (wall_clock64() - t0 > CH_WAIT_TICKS) {   // only when calls share a workspace
-                __hip_atomic_store(ws + CH_ERR, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
-            }
-          }
-        }
-        // acquire: this CU's caches drop lines that may predate the count
-        if (steal < 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_cmd = steal;
-      }
-      __syncthreads();
-      const int steal = uniform(s_cmd);
-      if (steal < 0) break;
-      first_tile(steal, drained);
-      __syncthreads();   // the ring is free again
-    }
-    run_tile<T, FWD2, false, false, false, W>(a2, gl, s2, t, smem, g_idx, drained);
   }
   // the last workgroup to finish (every draw and every publish of the
   // others done) returns the counters to zero for the next call
