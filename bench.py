@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=8192,
                    help="tokens in the oracle's timed sample")
     p.add_argument("--no-dense-ref", action="store_true",
-                   help="skip timing torch.matmul (hipBLASLt) on the dense equivalents")
+                   help="skip timing torch.matmul (hipBLASLt) on the dense equivalents and the "
+                        "reference HBM copies")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device-to-device copy of this many MiB before the timed "
                         "region (a known-size reference for HBM byte counters)")
@@ -201,6 +202,40 @@ def dense_reference(cfg, reps=10):
     return out
 
 
+def hbm_reference(reps=10):
+    """Reference HBM rates of plain torch kernels on this GPU, each timed with
+    HIP events after the same 1 GiB cache flush as the per-call breakdown: a
+    1 GiB device copy (1 GiB read + 1 GiB written) and a 1 GiB fill (write
+    only).  The copy gives the practical bar for the permute family, whose
+    calls mix reads and writes the same way."""
+    import torch
+    n = (1 << 30) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: b.copy_(a), 2 << 30),
+                             ("fill_1GiB", lambda: b.fill_(1.0), 1 << 30)):
+        fn()
+        ts = []
+        for _ in range(reps):
+            torch.amax(flush, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[reps // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    del a, b, flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(call):
     """HBM bytes per launch of ``call`` from the committed rocprofv3 byte
     counters, if they were taken on the current kernel source (else None)."""
@@ -345,6 +380,16 @@ def main():
             getattr(L, c)()
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
+    # the same calls back to back without the flush (inputs partly warm in
+    # the MALL from the call before, as in a step)
+    evw = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(len(timed))] for _ in range(args.steps)]
+    for s in range(args.steps):
+        for i, c in enumerate(timed):
+            evw[s][i][0].record(stream)
+            getattr(L, c)()
+            evw[s][i][1].record(stream)
+    torch.cuda.synchronize()
     del flush, sink
     L.overlap = overlap
     # median over the steps of each call's event-to-event time
@@ -354,6 +399,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T * args.steps / wall
 
+    per_call_warm = {c: float(np.median([evw[s][i][0].elapsed_time(evw[s][i][1])
+                                         for s in range(args.steps)]))
+                     for i, c in enumerate(timed)}
     alg = algorithmic(cfg, rows_local, active_local)
     phases = {}
     for c in timed:
@@ -366,16 +414,30 @@ def main():
         gbs = alg[c]["bytes"] / (ms * 1e-3) / 1e9
         d["gbs"] = round(gbs, 1)
         d["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        d["ms_warm"] = round(per_call_warm[c], 4)
+        d["frac_hbm_warm"] = round(alg[c]["bytes"] / (per_call_warm[c] * 1e-3) / 1e9
+                                   / HBM_PEAK_GBS, 4)
         phases[c] = d
     dom = max((c for c in calls if c.startswith("gmm")), key=lambda c: per_call[c])
     dom_call = "moe_grouped_gemm_" + dom[4:]
     traffic = measured_traffic(dom_call) if cfg.name == "pangu" else None
-    roof = {"kernel": f"{dom_call} (one call = 2 launches of gmm_kernel)",
-            "bound": "mfma", "achieved": phases[dom]["tflops"], "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": phases[dom]["frac_bf16_peak"],
+    launches = {"gmm_bwd": "2 persistent launches, gmm_pair_kernel [dact + SwiGLU bwd | dW2] "
+                           "then [dX | dW13]",
+                "gmm_fwd": "1 persistent launch, gmm_chain_kernel (gate/up + SwiGLU, then down)"}
+    # the binding roofline: whichever of the MFMA peak and HBM takes longer
+    # for the call's algorithmic flops and bytes
+    hbm_bound = alg[dom]["bytes"] / HBM_PEAK_GBS > alg[dom]["flops"] / BF16_PEAK_TFLOPS / 1e3
+    roof = {"kernel": f"{dom_call} ({launches.get(dom, 'one call')})",
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": phases[dom]["gbs"] if hbm_bound else phases[dom]["tflops"],
+            "peak": HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": phases[dom]["frac_hbm"] if hbm_bound else phases[dom]["frac_bf16_peak"],
             "traffic": round(traffic) if traffic else None,
             "flops_per_launch": alg[dom]["flops"], "ms_per_launch": round(per_call[dom], 4),
-            "algorithmic_bytes": alg[dom]["bytes"]}
+            "algorithmic_bytes": alg[dom]["bytes"],
+            "frac_bf16_peak": phases[dom]["frac_bf16_peak"],
+            "frac_hbm": phases[dom]["frac_hbm"]}
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -393,6 +455,7 @@ def main():
     }
     if not args.no_dense_ref and cfg.dtype == "bf16":
         out["dense_ref"] = dense_reference(cfg)
+        out["hbm_ref"] = hbm_reference()
     if not args.no_variants and cfg.dtype == "bf16":
         import math
         C = math.ceil(1.2 * cfg.T * cfg.k / cfg.E)   # capacity factor 1.2

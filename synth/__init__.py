@@ -82,6 +82,17 @@ CONFIGS = {
                           description="DeepSeek-V3-shaped full layer, heavy skew"),
     "stress": MoeConfig("stress", 16384, 7680, 256, 256, 8, "bf16", "none", router=False,
                         description="small-expert stress, logits drawn directly"),
+    # the per-device shape of the Pangu layer under expert parallelism after
+    # the all-to-all, with balanced peers: the 8 local experts receive T*k
+    # rows in all, T each (every token picks all 8 experts here, which gives
+    # exactly those group sizes), plus the shared expert on the T tokens
+    # (logits drawn directly: the router of that deployment runs over all
+    # 256 experts before the all-to-all, as in the pangu config)
+    "pangu_received": MoeConfig("pangu_received", 8192, 7680, 2048, 8, 8, "bf16", "none",
+                                router=False, shared=True,
+                                description="Pangu share as received under balanced EP: "
+                                            "8 local experts x T rows + shared, logits drawn "
+                                            "directly"),
 }
 
 
