@@ -432,3 +432,57 @@ def test_grouped_gemm_small_group_builds_are_bitwise_equal(abi, kind):
         assert torch.equal(a, b), name
     for a, b in zip(outs[0][:3], outs[0][5:]):
         assert torch.equal(a, b)
+
+
+def test_chained_forwards_on_two_streams(abi):
+    """Two chained forward launches at once, on two streams of the same
+    priority with a workspace each: every workgroup of one can be held up
+    while the other holds its CU, so this runs the protocol's no-deadlock
+    property on the hardware (a stuck wait gives up after one second and
+    sets the workspace's error word, which fails here rather than hanging).
+    Both results equal the same calls run one after the other, bit for bit,
+    over several rounds."""
+    r = _rng(777)
+    H, I = 1024, 512
+    probs = []
+    for counts in ([int(c) for c in r.integers(100, 900, 12)],
+                   [int(c) for c in r.integers(200, 1200, 10)]):
+        G = len(counts)
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+        R = int(offsets[-1])
+        tdt = torch.bfloat16
+        p = dict(G=G, R=R, OFF=dev(offsets, torch.int32),
+                 XP=dev(_store(r.standard_normal((R, H)), "bf16"), tdt),
+                 W13=dev(_store(r.standard_normal((G, 2 * I, H)) * 0.05, "bf16"), tdt),
+                 W2=dev(_store(r.standard_normal((G, H, I)) * 0.05, "bf16"), tdt))
+        probs.append(p)
+    wsb = abi.moe_gmm_workspace_bytes()
+
+    def outputs(p):
+        return [torch.zeros(p["R"], 2 * I, dtype=torch.bfloat16, device="cuda"),
+                torch.zeros(p["R"], I, dtype=torch.bfloat16, device="cuda"),
+                torch.zeros(p["R"], H, dtype=torch.bfloat16, device="cuda")]
+
+    def fwd(p, out, ws, stream=None):
+        abi.moe_grouped_gemm_fwd(p["XP"], p["OFF"], 0, p["G"], p["R"], abi.MOE_BF16, H, I,
+                                 p["W13"], p["W2"], *out, None, ws, wsb, stream)
+
+    wss = [torch.zeros(wsb, dtype=torch.uint8, device="cuda") for _ in probs]
+    ref = []
+    for p, ws in zip(probs, wss):
+        out = outputs(p)
+        fwd(p, out, ws)
+        ref.append(out)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(4):
+        got = [outputs(p) for p in probs]
+        torch.cuda.synchronize()
+        for p, out, ws, st in zip(probs, got, wss, streams):
+            fwd(p, out, ws, st)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
+        for ws in wss:   # counters back at zero, no wait gave up
+            assert int(ws.view(torch.int32).abs().sum()) == 0
