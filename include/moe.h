@@ -246,9 +246,9 @@ int moe_unpermute_combine_bwd(const void* dy, const void* yp, const int32_t* row
  * T rows in the same launch (a dense group with its own weights).
  * Arithmetic: dt products, fp32 accumulation; outputs stored as dt.
  *
- * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes (64 KiB plus
+ * Workspace: ws (nullable) of moe_gmm_workspace_bytes() bytes (320 KiB plus
  * 256), 256-byte aligned, holding the tile scheduler's counters and the
- * forward's per-row-tile completion counters.  It must be zero-filled before
+ * forward's per-row-tile completion counters and per-tile start words.  It must be zero-filled before
  * its first use; every call returns it to zero when it completes.  With it,
  * the workgroups of each XCD take their tiles from a shared counter (a
  * workgroup that starts late, e.g. while another kernel still holds its CU,
