@@ -1191,24 +1191,49 @@ __device__ __forceinline__ void persistent_loop(int* ctr, int total, int* s_next
   auto tile_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
   // ctr: [0, 8) per-XCD tile counters, [8] finished workgroups (NULL: static)
   const bool dyn = ctr != nullptr;
-  int k = wix;              // index of this workgroup's tile in the XCD's sequence
+  // thread 0, with the workspace: once the sequence of XCD vx (its own at
+  // first) is used up, the workgroup goes on drawing from the next XCD's
+  // counter, so XCDs that ran short tiles take the unstarted tiles of XCDs
+  // still busy with long ones (with a fixed sequence per XCD, the last
+  // round's long tiles landed on two XCDs while six others idled up to
+  // 170 us); every XCD's first wpx tiles are the static first tiles of its
+  // own workgroups
+  int vx = xcd;
+  auto pos_in = [&](int x, int k) { return (k / wpx) * nwg + x * wpx + k % wpx; };
+  auto resolve = [&](int k) {   // position of draw k of XCD vx's counter
+    int n = pos_in(vx, wpx + k);
+    for (int tries = 1; n >= total && tries < nx; ++tries) {
+      vx = (vx + 1) % nx;
+      n = pos_in(vx, wpx + __hip_atomic_fetch_add(ctr + vx, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT));
+    }
+    return n;
+  };
+  int k = wix;              // static order: index of the tile in the XCD's sequence
+  int n = tile_of(k);
   int grab = 0;             // thread 0: the counter value drawn at the start of this tile
   for (bool first = true;; first = false) {
     // every wave is done reading the ring (previous tile) and s_next holds
-    // the next tile; the previous tile's stores may still be draining --
-    // they overlap this tile's first copies (the copy waits count them
-    // too, which only makes them wait longer)
+    // the next tile's position; the previous tile's stores may still be
+    // draining -- they overlap this tile's first copies (the copy waits
+    // count them too, which only makes them wait longer)
     __syncthreads();
-    if (!first) k = dyn ? *s_next : k + wpx;
-    k = uniform(k);
-    const int n = tile_of(k);
+    if (!first) {
+      if (dyn) {
+        n = *s_next;
+      } else {
+        k += wpx;
+        n = tile_of(k);
+      }
+    }
+    n = uniform(n);
     if (n >= total) break;
     // draw the tile after this one now: the atomic returns long before its
     // value is read, at the epilogue's full wait
     if (dyn && tid == 0)
-      grab = __hip_atomic_fetch_add(ctr + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      grab = __hip_atomic_fetch_add(ctr + vx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     body(n, [&]() {
-      if (dyn && tid == 0) *s_next = wpx + grab;   // read after the next loop-top barrier
+      if (dyn && tid == 0) *s_next = resolve(grab);   // read after the next loop-top barrier
     });
   }
   // every draw of this workgroup has returned (the last one ended the loop);
@@ -1339,11 +1364,21 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_chain_kernel(GmmArgs a1, 
   const int nwg = gridDim.x;
   const int nx = (nwg % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx, wpx = nwg / nx;
-  int* const ctr = ws + CH_XCD + xcd;
-  // n-th position of this XCD's sequence
-  auto pos_of = [&](int n) { return (n / wpx) * nwg + xcd * wpx + n % wpx; };
+  // thread 0: the XCD whose sequence this workgroup draws from -- its own,
+  // then, once that is used up, the next XCD's (as in persistent_loop)
+  int vx = xcd;
   auto draw = [&]() {
-    return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(ws + CH_XCD + vx, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto pos_of = [&](int k) {   // position of draw k of XCD vx, moving on when it is used up
+    int c = (k / wpx) * nwg + vx * wpx + k % wpx;
+    for (int tries = 1; c >= total && tries < nx; ++tries) {
+      vx = (vx + 1) % nx;
+      const int k2 = draw();
+      c = (k2 / wpx) * nwg + vx * wpx + k2 % wpx;
+    }
+    return c;
   };
   auto take = [&](int t) {   // thread 0: start first-product tile t unless started
     return __hip_atomic_exchange(st + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;

@@ -4,7 +4,8 @@
 persistent launch: positions [0, total1) are gate/up tiles, [total1, total)
 down tiles; a down tile of row tile m may start only once every gate/up tile
 of m has finished.  The workgroups of each XCD take positions from their
-XCD's counter in blocks of ``wpx``; a workgroup owns a gate/up tile only
+XCD's counter in blocks of ``wpx``, and once that sequence is used up they
+go on with the next XCD's counter; a workgroup owns a gate/up tile only
 after exchanging its start word from 0 to 1, and a waiting down tile first
 runs every unstarted gate/up tile of its row tile itself.
 
@@ -45,15 +46,22 @@ def run(mt, nb1, nb2, nwg, seed, late=None):
     started2 = []
 
     def wg(b):
-        xcd = b % nx
-
-        def pos_of(n):
-            return (n // wpx) * nwg + xcd * wpx + n % wpx
+        vx = [b % nx]
 
         def draw():
-            v = ctr[xcd]
-            ctr[xcd] += 1
+            v = ctr[vx[0]]
+            ctr[vx[0]] += 1
             return v
+
+        def pos_of(k):
+            c = (k // wpx) * nwg + vx[0] * wpx + k % wpx
+            tries = 1
+            while c >= total and tries < nx:
+                vx[0] = (vx[0] + 1) % nx
+                k2 = draw()
+                c = (k2 // wpx) * nwg + vx[0] * wpx + k2 % wpx
+                tries += 1
+            return c
 
         def take(t):
             old, st[t] = st[t], 1
