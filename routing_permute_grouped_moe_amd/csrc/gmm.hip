@@ -92,7 +92,8 @@ struct GmmArgs {
   // dense groups: all G groups have rows [0, shT) and their own operands at
   // X + g*x_gs, W + g*w_gs, C + g*c_gs (elements); no offsets table
   int dense; long long x_gs;
-  int kwrap;     // > 0: the A operand's K index wraps with this period
+  int krep;      // > 1: each A K step serves krep consecutive K steps, whose
+                 // B rows differ (the parts of a split fp32 operand)
   int out_f32;   // plain-store epilogue writes fp32 whatever T is
   // tile scheduler counters (NULL: static tile order): 8 per-XCD tile
   // counters and a finished-workgroup counter, zero on entry and on exit
@@ -594,7 +595,8 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   const bool sh = g >= a.G;
   const bool gat = GATHER && !sh;   // routed tile of a gathering launch
   const long long xg = a.dense ? (long long)g * a.x_gs * ES : 0;   // dense group bases
-  const int arows = a.kwrap > 0 ? a.kwrap : kdim;   // A rows a DW tile can touch
+  const int krep = a.krep > 1 ? a.krep : 1;
+  const int arows = kdim / krep;   // A rows a DW tile can touch
 
   // ---- operand views
   View va, vb;
@@ -645,10 +647,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   else kmajor_offsets<T, MODE == FWD1, WS::WTN>(vb, n0, a.I, offb);
   const int sa = A_MN ? va.ld * BK * ES : BK * ES;   // uniform offset per K step
   const int sb = (GLOOP && gat) ? 0 : (B_MN ? vb.ld * BK * ES : BK * ES);
-  const int wrap_steps = a.kwrap > 0 ? a.kwrap / BK : 0x7fffffff;
   auto issue = [&](int kt) {
     const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    issue_op(va, st, offa, (kt % wrap_steps) * sa);
+    issue_op(va, st, offa, (kt / krep) * sa);
     issue_op(vb, st + OPB, offb, kt * sb);
   };
   // copy j of K step kt (j < DPA: operand A, else B); a step past the
@@ -657,9 +658,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
   const uint32_t lds_wa = lds_addr(smem) + (threadIdx.x >> 6) * DPA * 1024;
   const uint32_t lds_wb = lds_addr(smem) + OPB + (threadIdx.x >> 6) * DPB * 1024;
-  // (the A step index wraps for dW tiles that re-read a short operand;
-  // ka_next tracks kt % wrap_steps of the next step to issue)
-  int ka_next = 0;
+  // (the A step index is kt / krep; ka_next tracks it for the next step to
+  // issue, ka_rep the steps already issued from that A step)
+  int ka_next = 0, ka_rep = 0;
   auto issue1 = [&](int kt, int j) {
     const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
     const bool live = kt < KT;
@@ -667,7 +668,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       dma16(live ? va.rs : rs_none, lds_wa + so + j * 1024, offa[j], ka_next * sa);
     else
       dma16(live ? vb.rs : rs_none, lds_wb + so + (j - DPA) * 1024, offb[j - DPA], kt * sb);
-    if (j == DMA_PER_STEP - 1 && ++ka_next == wrap_steps) ka_next = 0;
+    if (j == DMA_PER_STEP - 1 && ++ka_rep == krep) { ka_rep = 0; ++ka_next; }
   };
   auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
   // GLOOP: B copy j of a step covers K rows 8 wave + 2 j + (0, 1), lane l
@@ -697,7 +698,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     const uint32_t vo =
         gat ? ((krow < kdim && offb[j] != OOB) ? iv[j] * rowb + offb[j] : OOB) : offb[j];
     dma16(kt < KT ? vb.rs : rs_none, lds_wb + so + j * 1024, vo, kt * sb);
-    if (j == DPB - 1 && ++ka_next == wrap_steps) ka_next = 0;
+    if (j == DPB - 1 && ++ka_rep == krep) { ka_rep = 0; ++ka_next; }
   };
 
   if (KT > 0) {
@@ -1971,7 +1972,7 @@ int moe_gmm_router_fwd(const void* x, const void* wg3s, float* partials, int T, 
                        hipStream_t s) {
   GmmArgs a = {};
   a.dense = 1; a.G = S; a.shT = T; a.R = T;
-  a.N = E; a.K = 3 * (H / S); a.kwrap = H / S;
+  a.N = E; a.K = 3 * (H / S); a.krep = 3;
   a.X = x; a.ldx = H; a.x_gs = H / S;
   a.W = wg3s; a.ldw = E; a.w_gs = 3LL * (H / S) * E;
   a.C = partials; a.ldc = E; a.c_gs = (long long)T * E; a.out_f32 = 1;
@@ -1993,7 +1994,7 @@ int moe_gmm_router_dwg(const void* x, const void* dl3s, float* partials, int T, 
                        hipStream_t s) {
   GmmArgs a = {};
   a.dense = 1; a.G = S; a.shT = 3 * (T / S); a.R = T;
-  a.M = H; a.N = E; a.kwrap = T / S;
+  a.M = H; a.N = E; a.krep = 3;
   a.X = x; a.ldx = H; a.x_gs = (long long)(T / S) * H;
   a.W = dl3s; a.ldw = E; a.w_gs = 3LL * (T / S) * E;
   a.C = partials; a.ldc = E; a.c_gs = (long long)H * E; a.out_f32 = 1;

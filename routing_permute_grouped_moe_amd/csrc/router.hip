@@ -147,41 +147,42 @@ __device__ __forceinline__ void split3(float v, uint32_t& h, uint32_t& m, uint32
   l = f32_to_bf16(r1 - bf16_to_f32(m));
 }
 
-// Wg [H,E] -> wg3s [S][3][H/S][E] (K rows of slice s: hi, mid, lo parts of
-// rows s*H/S .. ) and wgb [H,E] = hi part.
+// The K rows of slice s are taken 32 at a time (one K step of the GEMM):
+// the hi, mid and lo parts of a 32-row chunk follow each other, so the GEMM
+// reads each 32-deep step of its token operand once and multiplies it by the
+// three parts in consecutive K steps (krep = 3) while the step is in cache.
+#define RT_CHUNK 32
+
+// Wg [H,E] -> wg3s [S][H/S/32][3][32][E] and wgb [H,E] = hi part.
 __global__ __launch_bounds__(256) void split_wg_kernel(const float* __restrict__ wg, int H, int E,
                                                        bf16_t* __restrict__ wg3s,
                                                        bf16_t* __restrict__ wgb) {
   const long long n = (long long)H * E;
-  const int hs = H / RT_SPLIT;
   for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
     const int h = (int)(i / E), e = (int)(i % E);
     uint32_t p0, p1, p2;
     split3(wg[i], p0, p1, p2);
-    const int sl = h / hs, hl = h % hs;
-    const long long base = ((long long)sl * 3 * hs + hl) * E + e;
+    const long long base = ((long long)(h - h % RT_CHUNK) * 3 + h % RT_CHUNK) * E + e;
     wg3s[base] = (bf16_t)p0;
-    wg3s[base + (long long)hs * E] = (bf16_t)p1;
-    wg3s[base + 2LL * hs * E] = (bf16_t)p2;
+    wg3s[base + RT_CHUNK * E] = (bf16_t)p1;
+    wg3s[base + 2 * RT_CHUNK * E] = (bf16_t)p2;
     if (wgb) wgb[i] = (bf16_t)p0;
   }
 }
 
-// dl [T,E] -> dl3s [S][3][T/S][E] and dlb [T,E] = hi part.
+// dl [T,E] -> dl3s [S][T/S/32][3][32][E] and dlb [T,E] = hi part.
 __global__ __launch_bounds__(256) void split_dl_kernel(const float* __restrict__ dl, int T, int E,
                                                        bf16_t* __restrict__ dl3s,
                                                        bf16_t* __restrict__ dlb) {
   const long long n = (long long)T * E;
-  const int ts = T / RT_SPLIT;
   for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
     const int t = (int)(i / E), e = (int)(i % E);
     uint32_t p0, p1, p2;
     split3(dl[i], p0, p1, p2);
-    const int sl = t / ts, tl = t % ts;
-    const long long base = ((long long)sl * 3 * ts + tl) * E + e;
+    const long long base = ((long long)(t - t % RT_CHUNK) * 3 + t % RT_CHUNK) * E + e;
     dl3s[base] = (bf16_t)p0;
-    dl3s[base + (long long)ts * E] = (bf16_t)p1;
-    dl3s[base + 2LL * ts * E] = (bf16_t)p2;
+    dl3s[base + RT_CHUNK * E] = (bf16_t)p1;
+    dl3s[base + 2 * RT_CHUNK * E] = (bf16_t)p2;
     dlb[i] = (bf16_t)p0;
   }
 }
