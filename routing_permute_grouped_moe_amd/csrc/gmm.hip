@@ -1275,8 +1275,31 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
 // whose K (rows) is at least the row-tiled product's K run first, then the
 // row-tiled product, then the remaining (short) gradient tiles, which fill
 // the last round.
+//
+// Long tiles (the row-tiled product's and the leading gradient tiles) that
+// spill into a last partial round leave most workgroups idle at the end of
+// the first launch of a backward call (the short tiles fill only part of
+// it), so that launch keeps only as many leading gradient tiles as make its
+// long tiles a whole number of rounds; the second launch (a0.M > 0: a0 holds
+// the first launch's gradient product) runs the rest first.  Both launches
+// derive the split from the same group table, so every tile runs once.
+
+// leading gradient tiles: those of the groups with at least K rows
+__device__ __forceinline__ int lead_tiles(const GroupLds& gl, int ng, int K, const Space& s) {
+  int lead = 0;
+  while (lead < ng && gl.hi[gl.ord[lead]] - gl.lo[gl.ord[lead]] >= K) ++lead;
+  return lead * s.MBt * s.NBt;
+}
+// leading gradient tiles the first launch keeps: n1 row-tiled tiles plus the
+// kept ones a multiple of the P workgroups, if dropping at most L gets there
+__device__ __forceinline__ int lead_kept(int n1, int L, int P) {
+  const int over = (n1 + L) % P;
+  return over <= L ? L - over : L;
+}
+
 template <typename T, int M1, int M2, int W>
-__global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2) {
+__global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, GmmArgs a2,
+                                                                   GmmArgs a0) {
   static_assert(M1 != DW && M2 == DW, "a row-tiled product and a weight-gradient product");
   __shared__ __attribute__((aligned(1024))) char smem[RING_BYTES];
   __shared__ GroupLds gl;
@@ -1288,16 +1311,35 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, G
   group_order(ng, gl);
   const Space s1 = tile_space<M1, false>(a1, gl, &s_next);
   const Space s2 = tile_space<M2, false>(a2, gl, &s_next);
-  // leading gradient groups: K (rows) at least the row-tiled product's K
-  int lead = 0;
-  while (lead < ng && gl.hi[gl.ord[lead]] - gl.lo[gl.ord[lead]] >= a1.K) ++lead;
-  const int splitA = lead * s2.MBt * s2.NBt;
-  persistent_loop(a1.cnt, s1.total + s2.total, &s_next, [&](int n, auto&& drained) {
-    if (n >= splitA && n < splitA + s1.total)
-      run_row_tile<T, M1, false, true, W>(a1, gl, s1, n - splitA, smem, g_idx, drained);
-    else
-      run_tile<T, M2, false, false, true, W>(a2, gl, s2, n < splitA ? n : n - s1.total, smem,
-                                             g_idx, drained);
+  const int P = gridDim.x;
+  const bool second = a0.M > 0;
+  Space s0 = s2;
+  // positions: [mv tiles of a0 from tile t0][splitA gradient tiles][row-tiled
+  // product][gradient tiles from splitA + skip on]
+  int mv = 0, t0 = 0, splitA, skip = 0;
+  if (!second) {
+    const int L = lead_tiles(gl, ng, a1.K, s2);
+    splitA = lead_kept(s1.total, L, P);
+    skip = L - splitA;
+  } else {
+    s0 = tile_space<M2, false>(a0, gl, &s_next);
+    // the first launch's row-tiled product had K = a0.M and N = a0.N
+    const int n1 = gl.pre[ng] * ((a0.N + BN - 1) / BN);
+    const int L = lead_tiles(gl, ng, a0.M, s0);
+    t0 = lead_kept(n1, L, P);
+    mv = L - t0;
+    splitA = lead_tiles(gl, ng, a1.K, s2);
+  }
+  persistent_loop(a1.cnt, mv + s1.total + s2.total - skip, &s_next, [&](int n, auto&& drained) {
+    const int p = n - mv;
+    if (p >= splitA && p < splitA + s1.total) {
+      run_row_tile<T, M1, false, true, W>(a1, gl, s1, p - splitA, smem, g_idx, drained);
+    } else {
+      const bool f = p < 0;
+      const int t = f ? t0 + n : (p < splitA ? p : p - s1.total + skip);
+      run_tile<T, M2, false, false, true, W>(f ? a0 : a2, gl, f ? s0 : s2, t, smem, g_idx,
+                                             drained);
+    }
   });
 }
 
@@ -1540,15 +1582,19 @@ int launch(const GmmArgs& a, hipStream_t s, const char* what) {
   return moe_check_launch(what);
 }
 
+// a0: for the second launch of a backward call, the first launch's gradient
+// product (its leading tiles beyond the first launch's share run here);
+// M = 0 otherwise
 template <int M1, int M2>
-int launch_pair(int dt, const GmmArgs& a1, const GmmArgs& a2, hipStream_t s, const char* what) {
+int launch_pair(int dt, const GmmArgs& a1, const GmmArgs& a2, const GmmArgs& a0, hipStream_t s,
+                const char* what) {
   if (dt == MOE_BF16)
     hipLaunchKernelGGL((gmm_pair_kernel<bf16_t, M1, M2, WAVES<bf16_t, M1, false>>),
                        dim3(grid_size()), dim3(Waves<WAVES<bf16_t, M1, false>>::NT), 0, s, a1,
-                       a2);
+                       a2, a0);
   else
     hipLaunchKernelGGL((gmm_pair_kernel<float, M1, M2, 4>), dim3(grid_size()),
-                       dim3(Waves<4>::NT), 0, s, a1, a2);
+                       dim3(Waves<4>::NT), 0, s, a1, a2, a0);
   return moe_check_launch(what);
 }
 
@@ -1940,10 +1986,12 @@ extern "C" int moe_grouped_gemm_bwd(const void* xp, const void* act, const void*
   GmmArgs a2 = a1;
   dx1_args(a1, dyp, H, I, w2, h13, dh13, sh, sh_rows);
   dw2_args(a2, dyp, act, H, I, dw2, sh, sh_rows);
-  MOE_TRY((launch_pair<DX1, DW>(dt, a1, a2, s, fn)));
+  const GmmArgs none = {};
+  MOE_TRY((launch_pair<DX1, DW>(dt, a1, a2, none, s, fn)));
+  const GmmArgs a0 = a2;
   dx2_args(a1, H, I, w13, dh13, dxp, sh, sh_rows);
   dw13_args(a2, dh13, xp, H, I, dw13, sh, sh_rows);
-  return launch_pair<DX2, DW>(dt, a1, a2, s, fn);
+  return launch_pair<DX2, DW>(dt, a1, a2, a0, s, fn);
 }
 
 extern "C" int moe_grouped_gemm_bwd_dw_recompute(const void* x, const int32_t* src_token, int T,
