@@ -317,7 +317,9 @@ int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const void* dyp, co
  * persistent launches that each pair one dX product with the weight-gradient
  * product that does not depend on it -- [dact + SwiGLU bwd | dw2], then
  * [dxp | dw13] -- so the weight-gradient tiles fill the rounds the dX
- * products leave partly idle.  [Pangu-QA] keeps dW apart from dX so that dW
+ * products leave partly idle (the first launch keeps whole rounds of its
+ * long tiles; the dw2 tiles of the largest groups beyond that run at the
+ * start of the second).  [Pangu-QA] keeps dW apart from dX so that dW
  * can overlap communication; on one GPU it overlaps the dX products instead.
  * Shapes the paired launches do not cover (a shared expert with no rows, no
  * routed rows, groups averaging half a tile or less) run the two calls'

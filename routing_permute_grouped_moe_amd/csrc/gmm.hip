@@ -1939,7 +1939,8 @@ extern "C" int moe_grouped_gemm_bwd_dw(const void* xp, const void* act, const vo
 // dX and dW of one call: two persistent launches, each holding one product of
 // dX and one weight-gradient product that needs nothing from it --
 // [dact + SwiGLU bwd | dW2], then [dX | dW13] (dW13 reads the dh13 the first
-// launch wrote) -- so that neither dX product ends in a partial round of its
+// launch wrote; the second launch also runs the leading dW2 tiles the first
+// leaves to it) -- so that neither dX product ends in a partial round of its
 // own; every output is the same bits as moe_grouped_gemm_bwd_dx followed by
 // moe_grouped_gemm_bwd_dw.  Calls whose shapes the paired launches do not
 // cover (an empty shared expert, no rows, the small-group build) take the
