@@ -262,6 +262,10 @@ GMM_CASES = [
     # launches run several rounds of both products' tiles
     ([int(c) for c in np.random.default_rng(11).integers(100, 600, 40)], 512, 256, 0, None, 300,
      "bf16"),
+    # 86 groups of 300 rows (H = 256): 172 dact tiles and 86 leading dW2
+    # tiles are 258 long tiles, two past a round of a 256-workgroup grid, so
+    # the first backward launch leaves two leading dW2 tiles to the second
+    ([300] * 86, 256, 128, 0, None, 0, "bf16"),
     # the largest window: 1024 experts, most of them empty or tiny
     ([int(c) for c in np.random.default_rng(9).integers(0, 4, 1024) * (
         np.random.default_rng(10).random(1024) < 0.3)], 128, 64, 0, None, 0, "bf16"),
