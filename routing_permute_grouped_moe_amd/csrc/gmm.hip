@@ -530,7 +530,7 @@ __device__ __forceinline__ RowTile locate_row_tile(const GroupLds& gl, const Spa
 // index ring.  drained() runs once per tile, by every thread, at the point
 // where every copy of the tile and the scheduler's draw have landed.
 template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, bool ACT_DEV = false,
-          int WM = 2, typename Drained>
+          int WM = 2, bool DEEP = false, typename Drained>
 __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
                                          int tile_id, char* smem, int* g_idx, Drained&& drained) {
   using WS = Waves<W, WM>;
@@ -548,20 +548,30 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
                 "8 waves: bf16, without the gathered weight-gradient index ring");
   constexpr bool A_MN = (MODE == DW);
   constexpr bool B_MN = (MODE == DX1 || MODE == DX2 || MODE == DW);
-  constexpr int STAGES = Cfg<T>::STAGES, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
+  // DEEP (light builds, tiles of at most 64 rows): a stage holds only the
+  // A tile's first 64 rows (4 KB) beside the 16 KB B tile, so six stages fit
+  // the ring and five K steps are in flight instead of three.  Such a tile
+  // is bound by the latency of its weight stream (its few MFMAs and the
+  // copies of its padding rows are not what limits it), so more bytes in
+  // flight per CU is what speeds it up.  OPB: byte offset of the B tile in
+  // a stage.
+  static_assert(!DEEP || (LIGHT && WM == 2 && W == 4), "deep ring: light builds, 4 waves");
+  constexpr int STAGES = DEEP ? 6 : Cfg<T>::STAGES;
+  constexpr int OPB = DEEP ? 4096 : Cfg<T>::OPB;
+  constexpr int STAGE_BYTES = OPB + Cfg<T>::OPB;
   static_assert(WM == 2 || (WM == 1 && W == 4 && sizeof(T) == 2 && MODE != DW && !LIGHT),
                 "strip tiles: bf16 row-tiled products, 4 waves");
-  // buffer loads per wave per K step: DPA for the A tile (BMT rows), DPB for
-  // the B tile (256 rows or columns)
+  // buffer loads per wave per K step: DPA for the A tile (BMT rows; DEEP: 64),
+  // DPB for the B tile (256 rows or columns)
   constexpr int DPB = DPO_OF<T, W>;
-  constexpr int DPA = DPB * WM / 2;
+  constexpr int DPA = DEEP ? 1 : DPB * WM / 2;
   constexpr int DMA_PER_STEP = DPA + DPB;
   // MFMA slots of a half K step that issue the A (first half) and B (second
   // half) copies: right after the fragment loads, or the last slots where
   // a half step has fewer MFMAs than loads and copies
   constexpr int CS1 = (FM + FN < FM * FN - DPA) ? FM + FN : FM * FN - DPA;
   constexpr int CS2 = (FM + FN < FM * FN - DPB) ? FM + FN : FM * FN - DPB;
-  static_assert(STAGES * STAGE_BYTES == RING_BYTES, "stage ring size");
+  static_assert(STAGES * STAGE_BYTES <= RING_BYTES, "stage ring size");
   static_assert(BM * EP_PITCH * 4 <= RING_BYTES, "epilogue slice must fit the ring");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -703,7 +713,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
 
   if (KT > 0) {
     if constexpr (sizeof(T) == 2) {
-      // steps 0, 1 and 2 in flight (empty copies past the end), so the
+      // steps 0 .. STAGES-2 in flight (empty copies past the end), so the
       // wait counts below hold for every K step
       if constexpr (GLOOP) {
         // indices of steps 0-2 first; then per step A, B and the indices
@@ -728,7 +738,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
 #pragma unroll
           for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
       }
-      wait_vm<2 * DMA_PER_STEP + 2 * GI>();
+      wait_vm<(STAGES - 2) * DMA_PER_STEP + 2 * GI>();
     } else {
       for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
       if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
@@ -777,7 +787,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               if (q >= CS1 && q - CS1 < DPA) issue1(kt + STAGES - 1, q - CS1);
               __builtin_amdgcn_sched_barrier(0);
             }
-          wait_vm<DMA_PER_STEP + DPA + GI>();
+          wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA + GI>();
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -792,7 +802,17 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
             }
         }
       };
-      if constexpr (LIGHT) {
+      if constexpr (DEEP) {
+        // at most 64 rows: the upper waves hold padding only, the lower ones
+        // one or two fragments of rows
+        const int rw = rows - wm * WTM;
+        const int fa = uniform(rw <= 0 ? 0 : min(2, (rw + 31) / 32));
+        switch (fa) {
+          case 0: kloop(std::integral_constant<int, 0>{}); break;
+          case 1: kloop(std::integral_constant<int, 1>{}); break;
+          default: kloop(std::integral_constant<int, 2>{}); break;
+        }
+      } else if constexpr (LIGHT) {
         const int rw = rows - wm * WTM;             // rows of the tile in this wave's half
         const int fa = sp.light ? uniform(rw <= 0 ? 0 : min(FM, (rw + 31) / 32)) : FM;
         switch (fa) {
@@ -820,12 +840,12 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               __builtin_amdgcn_sched_barrier(0);
             }
           // K step kt+1 has landed once at most the copies issued after it
-          // (step kt+2, and step kt+3's A copies) are outstanding; the
-          // barrier extends that to all waves and retires every read of the
-          // stage refilled next
+          // (steps kt+2 .. kt+STAGES-2, and step kt+STAGES-1's A copies) are
+          // outstanding; the barrier extends that to all waves and retires
+          // every read of the stage refilled next
           // (GLOOP: also step kt+3's indices, issued right after step
           // kt+1's B copies, and one index copy more per step since)
-          wait_vm<DMA_PER_STEP + DPA + GI>();
+          wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA + GI>();
           __syncthreads();
           u32x4 ivn;
           if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
@@ -1262,10 +1282,19 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
   else group_order(ng, gl);
   const Space sp = tile_space<MODE, LIGHT>(a, gl, &s_next);
   persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained) {
-    if constexpr (MODE != DW && !LIGHT)   // (DX1 lean: both tile shapes fit the registers)
+    if constexpr (MODE != DW && !LIGHT) {   // (DX1 lean: both tile shapes fit the registers)
       run_row_tile<T, MODE, GATHER, MODE == DX1, W>(a, gl, sp, n, smem, g_idx, drained);
-    else
+    } else if constexpr (LIGHT && W == 4) {
+      // light loops in use: a tile of at most 64 rows takes the deep ring
+      // (DX1 lean, as above)
+      if (sp.light && uniform(locate_row_tile(gl, sp, ng, n).rows) <= 64)
+        run_tile<T, MODE, GATHER, true, MODE == DX1, W, false, 2, true>(a, gl, sp, n, smem,
+                                                                        g_idx, drained);
+      else
+        run_tile<T, MODE, GATHER, true, MODE == DX1, W>(a, gl, sp, n, smem, g_idx, drained);
+    } else {
       run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained);
+    }
   });
 }
 
