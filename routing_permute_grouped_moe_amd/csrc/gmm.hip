@@ -525,14 +525,104 @@ __device__ __forceinline__ RowTile locate_row_tile(const GroupLds& gl, const Spa
   return rt;
 }
 
+// Weight-gradient tile tile_id: its group (in descending row order), the
+// corner of its M x N block and the group's rows (the K range).
+struct DwLoc {
+  int g, m0, n0, rows0, kdim;
+};
+__device__ __forceinline__ DwLoc dw_locate(const GroupLds& gl, const Space& sp, int tile_id) {
+  const int per = sp.MBt * sp.NBt;   // tiles of one group
+  const int p = tile_id / per, local = tile_id % per;
+  DwLoc d;
+  d.g = gl.ord[p];
+  const int band = GM_BAND * sp.NBt;
+  const int sup = local / band, within = local % band;
+  const int first = sup * GM_BAND;
+  const int gsz = min(GM_BAND, sp.MBt - first);
+  d.m0 = (first + within % gsz) * BM;
+  d.n0 = (within / gsz) * BN;
+  d.rows0 = gl.lo[d.g];
+  d.kdim = gl.hi[d.g] - gl.lo[d.g];
+  return d;
+}
+// P and Q views of a weight-gradient tile (rows not gathered): the group's
+// K rows of X and of W (arows: the rows P can touch)
+template <typename T>
+__device__ __forceinline__ void dw_views(const GmmArgs& a, const DwLoc& d, int arows, View& va,
+                                         View& vb) {
+  constexpr int ES = Cfg<T>::ES;
+  const bool sh = d.g >= a.G;
+  const long long xg = a.dense ? (long long)d.g * a.x_gs * ES : 0;
+  const void* pb = sh ? a.sX : (const void*)((const char*)a.X + xg);
+  const void* qb =
+      sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)d.g * a.w_gs * ES : 0));
+  va = make_view((const char*)pb + (long long)d.rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
+                 a.ldx, a.M);
+  vb = make_view((const char*)qb + (long long)d.rows0 * a.ldw * ES, (long long)d.kdim * a.ldw * ES,
+                 a.ldw, a.N);
+}
+
+// Weight-gradient tiles overlap across tiles (bf16, 4 waves, rows not
+// gathered, bf16 output, one K step per A step): while a tile's epilogue
+// runs, the next tile's first two K steps are already being copied into
+// ring slots 2-3, and the epilogue stages its output through slots 0-1 in
+// two bf16 slices of 128 columns, so the copies are issued ahead of the
+// epilogue's stores and do not wait for them to drain (the vector-memory
+// counter retires in issue order).  A prefetched tile runs with its K step kt
+// in slot (kt + 2) % 4.  DW_STORES: buffer stores each thread issues in that
+// epilogue (2 slices x 16 chunks), which the prefetched tile's first waits
+// allow to be outstanding.
+constexpr int DW_STORES = 32;
+constexpr int DW_PRE = 2;   // K steps a weight-gradient tile's epilogue copies for the next
+__device__ __forceinline__ bool dw_overlap_ok(const GmmArgs& a) {
+  return !a.out_f32 && a.krep <= 1;
+}
+// Copies of K steps 0-1 of weight-gradient tile tile_id into slots 2-3, in
+// the order the tile's own prologue would issue them (every K step: the
+// DPO P copies, then the DPO Q copies; steps past the last through an empty
+// descriptor).
+template <typename T, int W>
+__device__ __forceinline__ void dw_prefetch(const GmmArgs& a, const GroupLds& gl, const Space& sp,
+                                            int tile_id, char* smem) {
+  constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK, OPB = Cfg<T>::OPB, STAGE_BYTES = 2 * OPB;
+  constexpr int DPO = DPO_OF<T, W>;
+  DwLoc d = dw_locate(gl, sp, tile_id);
+  d.g = uniform(d.g); d.m0 = uniform(d.m0); d.n0 = uniform(d.n0);
+  d.rows0 = uniform(d.rows0); d.kdim = uniform(d.kdim);
+  View va, vb;
+  dw_views<T>(a, d, d.kdim, va, vb);
+  uint32_t offa[DPO], offb[DPO];
+  mnmajor_offsets<T>(va, d.m0, offa);
+  mnmajor_offsets<T>(vb, d.n0, offb);
+  const int KT = (d.kdim + BK - 1) / BK;
+  const int sa = va.ld * BK * ES, sb = vb.ld * BK * ES;
+  const i32x4 rs_none = {0, 0, 0, MOE_RSRC_DW3};
+  const uint32_t lds_wa = lds_addr(smem) + (threadIdx.x >> 6) * DPO * 1024;
+  const uint32_t lds_wb = lds_addr(smem) + OPB + (threadIdx.x >> 6) * DPO * 1024;
+#pragma unroll
+  for (int kt = 0; kt < DW_PRE; ++kt) {
+    const uint32_t so = (uint32_t)((kt + DW_PRE) * STAGE_BYTES);
+#pragma unroll
+    for (int j = 0; j < DPO; ++j)
+      dma16(kt < KT ? va.rs : rs_none, lds_wa + so + j * 1024, offa[j], kt * sa);
+#pragma unroll
+    for (int j = 0; j < DPO; ++j)
+      dma16(kt < KT ? vb.rs : rs_none, lds_wb + so + j * 1024, offb[j], kt * sb);
+  }
+}
+struct NoPrefetch {
+  __device__ void operator()() const {}
+};
+
 // Tile tile_id of a product: main loop over K and epilogue.  smem is the
 // 128 KB operand ring (also the epilogue's staging), g_idx the gathered-row
 // index ring.  drained() runs once per tile, by every thread, at the point
 // where every copy of the tile and the scheduler's draw have landed.
 template <typename T, int MODE, bool GATHER, bool LIGHT, bool LEAN, int W, bool ACT_DEV = false,
-          int WM = 2, bool DEEP = false, typename Drained>
+          int WM = 2, bool DEEP = false, typename Drained, typename Prefetch = NoPrefetch>
 __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, const Space& sp,
-                                         int tile_id, char* smem, int* g_idx, Drained&& drained) {
+                                         int tile_id, char* smem, int* g_idx, Drained&& drained,
+                                         int pre_in = 0, Prefetch&& prefetch = Prefetch()) {
   using WS = Waves<W, WM>;
   constexpr int NT = WS::NT, WN = WS::WN, FN = WS::FN, HW = WS::HW, BMT = WS::BMT;
   constexpr int ES = Cfg<T>::ES, BK = Cfg<T>::BK;
@@ -556,6 +646,8 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   // flight per CU is what speeds it up.  OPB: byte offset of the B tile in
   // a stage.
   static_assert(!DEEP || (LIGHT && WM == 2 && W == 4), "deep ring: light builds, 4 waves");
+  // weight-gradient tiles that overlap across tiles (see dw_prefetch)
+  constexpr bool PF = MODE == DW && sizeof(T) == 2 && !GLOOP && W == 4 && WM == 2 && !DEEP;
   constexpr int STAGES = DEEP ? 6 : Cfg<T>::STAGES;
   constexpr int OPB = DEEP ? 4096 : Cfg<T>::OPB;
   constexpr int STAGE_BYTES = OPB + Cfg<T>::OPB;
@@ -588,17 +680,12 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     n0 = rt.nbi * ((MODE == FWD1) ? BN / 2 : BN);
     kdim = a.K;
   } else {
-    const int per = sp.MBt * sp.NBt;   // tiles of one group
-    const int p = tile_id / per, local = tile_id % per;
-    g = gl.ord[p];
-    const int band = GM_BAND * sp.NBt;
-    const int sup = local / band, within = local % band;
-    const int first = sup * GM_BAND;
-    const int gsz = min(GM_BAND, sp.MBt - first);
-    m0 = (first + within % gsz) * BM;
-    n0 = (within / gsz) * BN;
-    rows0 = gl.lo[g];
-    kdim = gl.hi[g] - gl.lo[g];
+    const DwLoc d = dw_locate(gl, sp, tile_id);
+    g = d.g;
+    m0 = d.m0;
+    n0 = d.n0;
+    rows0 = d.rows0;
+    kdim = d.kdim;
   }
   g = uniform(g); m0 = uniform(m0); n0 = uniform(n0);
   rows0 = uniform(rows0); rows = uniform(rows); kdim = uniform(kdim);
@@ -622,16 +709,14 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
     const int wcols = B_MN ? a.N : a.K;
     vb = make_view(wb, (long long)wrows * wcols * ES, a.ldw, a.N);
   } else {
-    const void* pb = sh ? a.sX : (const void*)((const char*)a.X + xg);
-    const void* qb = sh ? a.sW : (const void*)((const char*)a.W + (a.dense ? (long long)g * a.w_gs * ES : 0));
-    va = make_view((const char*)pb + (long long)rows0 * a.ldx * ES, (long long)arows * a.ldx * ES,
-                   a.ldx, a.M);
+    dw_views<T>(a, DwLoc{g, m0, n0, rows0, kdim}, arows, va, vb);
     if (gat)   // DW: Q's K rows are gathered from the whole token matrix
       vb = make_view(a.W, (long long)a.gather_rows * a.ldw * ES, a.ldw, a.N);
-    else
-      vb = make_view((const char*)qb + (long long)rows0 * a.ldw * ES,
-                     (long long)kdim * a.ldw * ES, a.ldw, a.N);
   }
+  // a weight-gradient tile whose first K steps the previous tile's epilogue
+  // copied (slots 2-3): its K step kt lives in slot (kt + 2) % 4
+  const bool pf_ok = PF && dw_overlap_ok(a);
+  const int pre = uniform((PF && pre_in) ? DW_PRE : 0);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -670,9 +755,9 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   const uint32_t lds_wb = lds_addr(smem) + OPB + (threadIdx.x >> 6) * DPB * 1024;
   // (the A step index is kt / krep; ka_next tracks it for the next step to
   // issue, ka_rep the steps already issued from that A step)
-  int ka_next = 0, ka_rep = 0;
+  int ka_next = pre, ka_rep = 0;   // (prefetched: steps 0 .. pre-1 issued)
   auto issue1 = [&](int kt, int j) {
-    const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
+    const uint32_t so = (uint32_t)(((kt + pre) % STAGES) * STAGE_BYTES);
     const bool live = kt < KT;
     if (j < DPA)
       dma16(live ? va.rs : rs_none, lds_wa + so + j * 1024, offa[j], ka_next * sa);
@@ -680,7 +765,7 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       dma16(live ? vb.rs : rs_none, lds_wb + so + (j - DPA) * 1024, offb[j - DPA], kt * sb);
     if (j == DMA_PER_STEP - 1 && ++ka_rep == krep) { ka_rep = 0; ++ka_next; }
   };
-  auto stage = [&](int kt) { return (const char*)smem + (kt % STAGES) * STAGE_BYTES; };
+  auto stage = [&](int kt) { return (const char*)smem + ((kt + pre) % STAGES) * STAGE_BYTES; };
   // GLOOP: B copy j of a step covers K rows 8 wave + 2 j + (0, 1), lane l
   // the row l / 32.  The indices of a wave's 8 rows of step kt are copied
   // to its slot kt % 4 in the order 0 2 4 6 1 3 5 7, so a lane's four
@@ -735,10 +820,18 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       } else {
 #pragma unroll
         for (int kt = 0; kt < STAGES - 1; ++kt)
+          if (kt >= pre)
 #pragma unroll
-          for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
+            for (int j = 0; j < DMA_PER_STEP; ++j) issue1(kt, j);
       }
-      wait_vm<(STAGES - 2) * DMA_PER_STEP + 2 * GI>();
+      // (prefetched: the previous tile's epilogue stores were issued after
+      // steps 0-1, so they may still be outstanding here)
+      if constexpr (PF) {
+        if (pre) wait_vm<(STAGES - 2) * DMA_PER_STEP + DW_STORES>();
+        else wait_vm<(STAGES - 2) * DMA_PER_STEP>();
+      } else {
+        wait_vm<(STAGES - 2) * DMA_PER_STEP + 2 * GI>();
+      }
     } else {
       for (int kt = 0; kt < STAGES - 1 && kt < KT; ++kt) issue(kt);
       if (KT >= 3) wait_vm<2 * DMA_PER_STEP>();
@@ -845,7 +938,14 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
           // every read of the stage refilled next
           // (GLOOP: also step kt+3's indices, issued right after step
           // kt+1's B copies, and one index copy more per step since)
-          wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA + GI>();
+          // (prefetched tile, step 0: the previous tile's epilogue stores,
+          // issued after step 1, may still be outstanding)
+          if constexpr (PF) {
+            if (pre && kt == 0) wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA + DW_STORES>();
+            else wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA>();
+          } else {
+            wait_vm<(STAGES - 3) * DMA_PER_STEP + DPA + GI>();
+          }
           __syncthreads();
           u32x4 ivn;
           if constexpr (GLOOP) ivn = read_idx(kt + STAGES - 1);
@@ -903,6 +1003,58 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
   wait_vm<0>();      // the empty copies past the last step (and the draw) have landed
   drained();   // the scheduler's draw has returned: publish the next tile
   __syncthreads();   // every wave is done with the ring
+  if constexpr (PF) {
+    if (pf_ok) {
+      // the next tile's first K steps into slots 2-3 (if it is a weight-
+      // gradient tile of this launch), ahead of this tile's stores
+      prefetch();
+      // the output leaves through slots 0-1 in two bf16 slices: slice h
+      // holds fragments 2h and 2h+1 of every wave, LDS column c (of 128) =
+      // wn * 64 + the column in those two fragments, i.e. tile column
+      // wn * WTN + 64 h + c % 64; 16-byte unit u of row r sits at u ^ (r & 15).
+      // Rounded to bf16 once, as the plain store rounds.
+      const int m = elane & 31;
+      void* cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * ES);
+      const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, out_bytes((long long)a.M * a.ldc * ES));
+      char* const sl = smem;
+      auto slice2 = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int row = wm * WTM + f * 32 + m;
+              const int c = wn * 64 + j * 32 + rq * 8 + (elane >> 5) * 4;
+              // (the empty asm keeps each conversion at its store: converted
+              // ahead of time, the whole tile's bf16 values would not fit the
+              // registers)
+              float x0 = acc[f][2 * h + j][rq * 4 + 0], x1 = acc[f][2 * h + j][rq * 4 + 1];
+              float x2 = acc[f][2 * h + j][rq * 4 + 2], x3 = acc[f][2 * h + j][rq * 4 + 3];
+              asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+              u32x2 v;
+              v.x = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
+              v.y = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
+              *(u32x2*)(sl + row * 256 + (((c >> 3) ^ (row & 15)) << 4) + ((c >> 2) & 1) * 8) = v;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 256 * 16 / NT; ++it) {
+          const int idx = it * NT + etid;
+          const int row = idx >> 4, u = idx & 15;
+          const u32x4 v = *(const u32x4*)(sl + row * 256 + ((u ^ (row & 15)) << 4));
+          const int n = n0 + (u >> 3) * WS::WTN + 64 * h + (u & 7) * 8;
+          const int mm = m0 + row;
+          buf_store16_nt(cr, (mm < a.M && n < a.N) ? (uint32_t)(mm * a.ldc + n) * 2u : DROP, v);
+        }
+        __syncthreads();
+      };
+      slice2(std::integral_constant<int, 0>{});
+      slice2(std::integral_constant<int, 1>{});
+      return;
+    }
+  }
   float* ep = (float*)smem;
   auto put = [&](auto fn0c, auto&& value) {
     // fragments fn0 .. fn0 + FN/2 - 1 of each wave -> LDS columns
@@ -1199,8 +1351,10 @@ __device__ __forceinline__ void run_row_tile(const GmmArgs& a, const GroupLds& g
 // workgroup w of an XCD takes the w-th tile of each of its blocks; with one
 // the XCD's workgroups draw its tiles in order from the XCD's counter, so a
 // workgroup that starts late (its CU was still busy with another kernel) or
-// drew short tiles just takes fewer or more.  body(n, drained) runs the n-th
-// tile of the launch's sequence of total tiles.
+// drew short tiles just takes fewer or more.  body(n, drained, peek) runs the
+// n-th tile of the launch's sequence of total tiles; peek() gives the
+// position of the workgroup's next tile (>= total: none) once drained() has
+// run and a barrier has followed.
 template <typename Body>
 __device__ __forceinline__ void persistent_loop(int* ctr, int total, int* s_next, Body&& body) {
   const int tid = threadIdx.x;
@@ -1253,9 +1407,14 @@ __device__ __forceinline__ void persistent_loop(int* ctr, int total, int* s_next
     // value is read, at the epilogue's full wait
     if (dyn && tid == 0)
       grab = __hip_atomic_fetch_add(ctr + vx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    body(n, [&]() {
-      if (dyn && tid == 0) *s_next = resolve(grab);   // read after the next loop-top barrier
-    });
+    body(
+        n,
+        [&]() {
+          if (dyn && tid == 0) *s_next = resolve(grab);   // read after the next loop-top barrier
+        },
+        // the next tile's position, once drained() has run and a barrier
+        // has followed it (what the next loop top reads)
+        [&]() { return uniform(dyn ? *s_next : tile_of(k + wpx)); });
   }
   // every draw of this workgroup has returned (the last one ended the loop);
   // the last workgroup to finish returns the counters to zero for the next call
@@ -1281,7 +1440,8 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
   if constexpr (MODE != DW) tile_prefix(ng, gl);
   else group_order(ng, gl);
   const Space sp = tile_space<MODE, LIGHT>(a, gl, &s_next);
-  persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained) {
+  int pre = 0;   // this workgroup's next tile has its first K steps in the ring
+  persistent_loop(a.cnt, sp.total, &s_next, [&](int n, auto&& drained, auto&& peek) {
     if constexpr (MODE != DW && !LIGHT) {   // (DX1 lean: both tile shapes fit the registers)
       run_row_tile<T, MODE, GATHER, MODE == DX1, W>(a, gl, sp, n, smem, g_idx, drained);
     } else if constexpr (LIGHT && W == 4) {
@@ -1292,6 +1452,16 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_kernel(GmmArgs a) {
                                                                         g_idx, drained);
       else
         run_tile<T, MODE, GATHER, true, MODE == DX1, W>(a, gl, sp, n, smem, g_idx, drained);
+    } else if constexpr (MODE == DW && sizeof(T) == 2 && !GLOOP && W == 4) {
+      const int pr = pre;
+      pre = 0;
+      run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained, pr, [&]() {
+        const int nn = peek();
+        if (nn < sp.total) {
+          dw_prefetch<T, W>(a, gl, sp, nn, smem);
+          pre = 1;
+        }
+      });
     } else {
       run_tile<T, MODE, GATHER, LIGHT, false, W>(a, gl, sp, n, smem, g_idx, drained);
     }
@@ -1359,15 +1529,30 @@ __global__ __launch_bounds__(Waves<W>::NT, 1) void gmm_pair_kernel(GmmArgs a1, G
     mv = L - t0;
     splitA = lead_tiles(gl, ng, a1.K, s2);
   }
-  persistent_loop(a1.cnt, mv + s1.total + s2.total - skip, &s_next, [&](int n, auto&& drained) {
+  const int total = mv + s1.total + s2.total - skip;
+  int pre = 0;   // this workgroup's next (gradient) tile has its first K steps in the ring
+  persistent_loop(a1.cnt, total, &s_next, [&](int n, auto&& drained, auto&& peek) {
     const int p = n - mv;
     if (p >= splitA && p < splitA + s1.total) {
       run_row_tile<T, M1, false, true, W>(a1, gl, s1, p - splitA, smem, g_idx, drained);
     } else {
       const bool f = p < 0;
       const int t = f ? t0 + n : (p < splitA ? p : p - s1.total + skip);
-      run_tile<T, M2, false, false, true, W>(f ? a0 : a2, gl, f ? s0 : s2, t, smem, g_idx,
-                                             drained);
+      const int pr = pre;
+      pre = 0;
+      run_tile<T, M2, false, false, true, W>(
+          f ? a0 : a2, gl, f ? s0 : s2, t, smem, g_idx, drained, pr, [&]() {
+            if constexpr (sizeof(T) == 2 && W == 4) {
+              const int nn = peek();
+              const int pp = nn - mv;
+              if (nn < total && !(pp >= splitA && pp < splitA + s1.total)) {
+                const bool ff = pp < 0;
+                const int tt = ff ? t0 + nn : (pp < splitA ? pp : pp - s1.total + skip);
+                dw_prefetch<T, W>(ff ? a0 : a2, gl, ff ? s0 : s2, tt, smem);
+                pre = 1;
+              }
+            }
+          });
     }
   });
 }
