@@ -1011,8 +1011,10 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
       // the output leaves through slots 0-1 in two bf16 slices: slice h
       // holds fragments 2h and 2h+1 of every wave, LDS column c (of 128) =
       // wn * 64 + the column in those two fragments, i.e. tile column
-      // wn * WTN + 64 h + c % 64; 16-byte unit u of row r sits at u ^ (r & 15).
-      // Rounded to bf16 once, as the plain store rounds.
+      // wn * WTN + 64 h + c % 64; 16-byte unit u of row r sits at u ^ (r & 15)
+      // with its two 8-byte halves swapped where bits 3 and 4 of r differ, so
+      // the rows of a fragment's write hit distinct banks 16 or 32 lanes at a
+      // time.  Rounded to bf16 once, as the plain store rounds.
       const int m = elane & 31;
       void* cb = sh ? a.sC : (void*)((char*)a.C + (long long)g * a.c_gs * ES);
       const __amdgpu_buffer_rsrc_t cr = make_rsrc(cb, out_bytes((long long)a.M * a.ldc * ES));
@@ -1036,14 +1038,16 @@ __device__ __forceinline__ void run_tile(const GmmArgs& a, const GroupLds& gl, c
               u32x2 v;
               v.x = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
               v.y = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
-              *(u32x2*)(sl + row * 256 + (((c >> 3) ^ (row & 15)) << 4) + ((c >> 2) & 1) * 8) = v;
+              *(u32x2*)(sl + row * 256 + (((c >> 3) ^ (row & 15)) << 4) +
+                        ((((c >> 2) ^ (row >> 3) ^ (row >> 4)) & 1) * 8)) = v;
             }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < 256 * 16 / NT; ++it) {
           const int idx = it * NT + etid;
           const int row = idx >> 4, u = idx & 15;
-          const u32x4 v = *(const u32x4*)(sl + row * 256 + ((u ^ (row & 15)) << 4));
+          u32x4 v = *(const u32x4*)(sl + row * 256 + ((u ^ (row & 15)) << 4));
+          if (((row >> 3) ^ (row >> 4)) & 1) v = u32x4{v.z, v.w, v.x, v.y};
           const int n = n0 + (u >> 3) * WS::WTN + 64 * h + (u & 7) * 8;
           const int mm = m0 + row;
           buf_store16_nt(cr, (mm < a.M && n < a.N) ? (uint32_t)(mm * a.ldc + n) * 2u : DROP, v);
